@@ -1,0 +1,242 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code with the HIP library.
+ *
+ * What it computes (the plain definition, no blocking, no online state):
+ *
+ *   For each (batch b, head h, query i), with a scale s,
+ *     S_ij   = s * (q_i . k_j)                        for every valid key j
+ *     m_i    = max_j S_ij                             (pass 1)
+ *     l_i    = sum_j exp(S_ij - m_i)                  (pass 2)
+ *     O_i    = sum_j exp(S_ij - m_i) * v_j / l_i      (pass 3)
+ *     LSE_i  = m_i + ln(l_i)
+ *
+ *   - "Flash Attention 4" (mlc.ai, section "algorithm structure"): the
+ *     definitions of s_ij, the per-row maximum, p_ij, l_i, o_i and O_i = o_i/l_i;
+ *     FlashAttention returns the same result as standard attention.
+ *   - "Flash Attention记录" (zhen8838), section "SoftMax": the safe softmax
+ *     that subtracts the row maximum before exponentiating, in three passes.
+ *   - "FlashAttention：一次前向计算" (qingsen), section "what attention
+ *     computes": S = QK^T, P = rowwise softmax(sS), O = PV with an explicit
+ *     scale s; section "general update": L_i = s*m_i + log(l_i) where m_i is
+ *     the maximum of the unscaled scores (same value as m_i + ln l_i here,
+ *     because this file keeps the scores already scaled).
+ *
+ * Valid keys (causal masking): "Flash Attention 4", section "Causal Mask":
+ * with Nq queries and Nk keys the mask is aligned to the bottom-right corner,
+ * so query i may use keys j <= i + Nk - Nq (clamped to Nk - 1).  A row with
+ * no valid key has O = 0 ("algorithm structure": O is 0 when the row sum is
+ * 0) and LSE = -inf ("rescale and write-back": rows without a valid key).
+ *
+ * Layouts (all row-major, contiguous, fp64):
+ *   fixed length : q [B, Nq, H, d]; k, v [B, Nk, H, d]; o [B, Nq, H, d];
+ *                  lse [B, H, Nq]
+ *   packed varlen: q, k, v, o [T, H, d] with sequence b occupying tokens
+ *                  offsets[b] .. offsets[b+1]-1 (self attention, Nq = Nk = L_b);
+ *                  lse [H, T]
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Number of keys query i may use. */
+static int64_t valid_keys(int64_t i, int64_t Nq, int64_t Nk, int causal)
+{
+    if (!causal) return Nk;
+    int64_t last = i + Nk - Nq;          /* largest usable key index */
+    if (last < 0) return 0;
+    if (last >= Nk) return Nk;
+    return last + 1;
+}
+
+/*
+ * One query row.  qi points at d values; key j starts at k + j*stride,
+ * value j at v + j*stride.  s_buf must hold nvalid doubles.
+ */
+static void attention_row(const double *qi, const double *k, const double *v,
+                          int64_t stride, int64_t nvalid, int64_t d,
+                          double scale, double *s_buf, double *out, double *lse)
+{
+    if (nvalid <= 0) {
+        for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    /* pass 1: scaled scores and their maximum */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvalid; ++j) {
+        const double *kj = k + j * stride;
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kj[c];
+        s_buf[j] = scale * dot;
+        if (s_buf[j] > m) m = s_buf[j];
+    }
+    /* pass 2: denominator relative to the maximum */
+    double l = 0.0;
+    for (int64_t j = 0; j < nvalid; ++j) l += exp(s_buf[j] - m);
+    /* pass 3: normalised weighted sum of the value rows */
+    for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t j = 0; j < nvalid; ++j) {
+        double p = exp(s_buf[j] - m) / l;
+        const double *vj = v + j * stride;
+        for (int64_t c = 0; c < d; ++c) out[c] += p * vj[c];
+    }
+    *lse = m + log(l);
+}
+
+/* Fixed-length batch, every row.  Returns 0, or -1 on bad arguments. */
+int oracle_attn_fwd(const double *q, const double *k, const double *v,
+                    double *o, double *lse,
+                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    double scale, int causal)
+{
+    if (!q || !k || !v || !o || !lse || B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0)
+        return -1;
+    const int64_t stride = H * d;
+    const int64_t nrows = B * H * Nq;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        if (!s_buf) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t i = r % Nq;
+                int64_t h = (r / Nq) % H;
+                int64_t b = r / (Nq * H);
+                const double *qi = q + ((b * Nq + i) * H + h) * d;
+                const double *kb = k + (b * Nk * H + h) * d;
+                const double *vb = v + (b * Nk * H + h) * d;
+                attention_row(qi, kb, vb, stride, valid_keys(i, Nq, Nk, causal), d, scale,
+                              s_buf, o + ((b * Nq + i) * H + h) * d,
+                              lse + (b * H + h) * Nq + i);
+            }
+            free(s_buf);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* Packed variable-length batch of nseq sequences, every row. */
+int oracle_attn_fwd_varlen(const double *q, const double *k, const double *v,
+                           double *o, double *lse,
+                           int64_t nseq, const int64_t *offsets, int64_t H, int64_t d,
+                           double scale, int causal)
+{
+    if (!q || !k || !v || !o || !lse || !offsets || nseq < 0 || H < 0 || d <= 0)
+        return -1;
+    const int64_t T = offsets[nseq];
+    int64_t maxlen = 0;
+    for (int64_t b = 0; b < nseq; ++b) {
+        int64_t L = offsets[b + 1] - offsets[b];
+        if (L < 0) return -1;
+        if (L > maxlen) maxlen = L;
+    }
+    const int64_t stride = H * d;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1));
+        if (!s_buf) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < T * H; ++r) {
+                int64_t h = r % H;
+                int64_t t = r / H;
+                int64_t b = 0;
+                while (offsets[b + 1] <= t) ++b;
+                int64_t start = offsets[b];
+                int64_t L = offsets[b + 1] - start;
+                int64_t i = t - start;
+                attention_row(q + (t * H + h) * d, k + (start * H + h) * d,
+                              v + (start * H + h) * d, stride,
+                              valid_keys(i, L, L, causal), d, scale, s_buf,
+                              o + (t * H + h) * d, lse + h * T + t);
+            }
+            free(s_buf);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * A chosen subset of rows.  rows holds nrows triples (b, h, i).  Without
+ * offsets the layout is the fixed-length one with sizes Nq, Nk; with offsets
+ * (nseq+1 entries) the layout is the packed one and b names a sequence, i a
+ * position inside it.  Results go to o_out [nrows, d] and lse_out [nrows].
+ */
+int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
+                         int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                         double scale, int causal,
+                         const int64_t *offsets, int64_t nseq,
+                         int64_t nrows, const int64_t *rows,
+                         double *o_out, double *lse_out)
+{
+    if (!q || !k || !v || !rows || !o_out || !lse_out || H <= 0 || d <= 0 || nrows < 0)
+        return -1;
+    int64_t maxkeys = Nk;
+    if (offsets) {
+        maxkeys = 0;
+        for (int64_t b = 0; b < nseq; ++b) {
+            int64_t L = offsets[b + 1] - offsets[b];
+            if (L > maxkeys) maxkeys = L;
+        }
+    }
+    const int64_t stride = H * d;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(maxkeys > 0 ? maxkeys : 1));
+        if (!s_buf) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+                const double *qi, *kb, *vb;
+                int64_t nvalid;
+                if (offsets) {
+                    if (b < 0 || b >= nseq) {
+#pragma omp atomic write
+                        bad = 1;
+                        continue;
+                    }
+                    int64_t start = offsets[b], L = offsets[b + 1] - offsets[b];
+                    if (h < 0 || h >= H || i < 0 || i >= L) {
+#pragma omp atomic write
+                        bad = 1;
+                        continue;
+                    }
+                    qi = q + ((start + i) * H + h) * d;
+                    kb = k + (start * H + h) * d;
+                    vb = v + (start * H + h) * d;
+                    nvalid = valid_keys(i, L, L, causal);
+                } else {
+                    if (h < 0 || h >= H || i < 0 || i >= Nq || b < 0) {
+#pragma omp atomic write
+                        bad = 1;
+                        continue;
+                    }
+                    qi = q + ((b * Nq + i) * H + h) * d;
+                    kb = k + (b * Nk * H + h) * d;
+                    vb = v + (b * Nk * H + h) * d;
+                    nvalid = valid_keys(i, Nq, Nk, causal);
+                }
+                attention_row(qi, kb, vb, stride, nvalid, d, scale, s_buf,
+                              o_out + r * d, lse_out + r);
+            }
+            free(s_buf);
+        }
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,52 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pins catch every one of them.  This shows the pins constrain each part of
+the oracle: the scale, the maximum subtraction, the normaliser, the key/value
+strides, the mask alignment and the LSE."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "drop_scale": ("s_buf[j] = scale * dot;", "s_buf[j] = dot;"),
+    "sum_without_max": ("l += exp(s_buf[j] - m);", "l += exp(s_buf[j]);"),
+    "no_normalise": ("double p = exp(s_buf[j] - m) / l;", "double p = exp(s_buf[j] - m);"),
+    "key_stride_d": ("const double *kj = k + j * stride;", "const double *kj = k + j * d;"),
+    "values_from_keys": ("const double *vj = v + j * stride;", "const double *vj = k + j * stride;"),
+    "causal_off_by_one": ("return last + 1;", "return last;"),
+    "top_left_alignment": ("int64_t last = i + Nk - Nq;", "int64_t last = i;"),
+    "lse_without_max": ("*lse = m + log(l);", "*lse = log(l);"),
+    "empty_row_lse_zero": ("*lse = -INFINITY;", "*lse = 0.0;"),
+    "key_head_offset_dropped": ("const double *kb = k + (b * Nk * H + h) * d;",
+                                "const double *kb = k + (b * Nk * H) * d;"),
+    "lse_wrong_slot": ("lse + (b * H + h) * Nq + i);", "lse + (h * B + b) * Nq + i);"),
+}
+
+
+def _run_pins(orc):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as exc:  # a crash or NaN counts as caught
+            failed.append((pin.__name__, type(exc).__name__))
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path = tmp_path / f"oracle_{name}.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / f"liboracle_{name}.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(path), "-lm"],
+                   check=True)
+    failed = _run_pins(oracle.Oracle(str(so)))
+    assert failed, f"mutant {name} passed every pin"
