@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention forward on one MI355X.
+
+A step is one fa_fwd call: the whole forward (tile scheduling, Q/K/V loads,
+S = QK^T, masking, online softmax with conditional rescale, O += PV, epilogue)
+runs in one kernel launch on inputs already resident in HBM.  The default
+workload is causal attention, B=2, H=32, Nq=Nk=4096, d=128, bf16 in, bf16 O,
+fp32 LSE, scale 1/sqrt(128), seeded N(0,1) inputs.
+
+Prints one JSON line:
+  value        TFLOP/s = 4*B*H*Nq*Nk*d/2 (causal) / ms_per_step
+  roofline     the kernel's achieved TFLOP/s from per-launch HIP events on the
+               launch stream, against the bf16 dense MFMA peak (2.5 PFLOP/s);
+               traffic = HBM bytes per launch from the committed rocprofv3
+               FETCH_SIZE / WRITE_SIZE summary (null unless it was taken on the
+               kernel source as it is now)
+  cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same
+               workload (whole (batch, head) slices until ~10 s have passed)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["flashattention_forward_fa_amd/csrc/fa_fwd_kernel.hip",
+                  "flashattention_forward_fa_amd/csrc/fa_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from profiles/<workload>.pmc.txt, or None when the
+    counters were taken on another kernel source."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}.pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(re.findall(r"^([a-z_]+):\s*(\S+)\s*$", text, flags=re.M))
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the oracle on whole (sequence, head) slices of the workload until budget_s."""
+    import oracle
+    from flashattention_forward_fa_amd import workloads as wl
+    orc = oracle.default()
+    d = w.d
+    if w.varlen:
+        units = [(b, h) for h in range(w.H) for b in range(len(w.lengths))]
+    else:
+        units = [(b, h) for h in range(w.H) for b in range(w.B)]
+    flops = 0.0
+    spent = 0.0
+    done = 0
+    for (b, h) in units:
+        if w.varlen:
+            sl = slice(int(w.offsets[b]), int(w.offsets[b + 1]))
+            pick = lambda x: wl.bf16_to_f64(x[sl, h:h + 1])[None]
+            Nq = Nk = int(w.lengths[b])
+        else:
+            pick = lambda x: wl.bf16_to_f64(x[b:b + 1, :, h:h + 1])
+            Nq, Nk = w.Nq, w.Nk
+        q, k, v = pick(w.q), pick(w.k), pick(w.v)
+        t0 = time.perf_counter()
+        orc.attention(q, k, v, w.scale, w.causal)
+        spent += time.perf_counter() - t0
+        per = 4.0 * Nq * Nk * d
+        flops += per / 2.0 if w.causal else per
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, head) slices, every query row of each, "
+                      f"fp64 three-pass, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload 1-5 (3 = the headline)")
+    ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the oracle CPU baseline (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the forward shards over (batch, head) with no exchange; run one process per GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import flashattention_forward_fa_amd as fa
+    from flashattention_forward_fa_amd import workloads as wl
+    from tests import parity
+
+    torch.cuda.set_device(0)
+    fa.load()
+    w = wl.config(args.config)
+    q, k, v, off = parity.to_device(w)
+    odt = fa.FA_DTYPE_F32 if w.o_dtype == "f32" else fa.FA_DTYPE_BF16
+    o = torch.empty(q.shape, dtype=torch.float32 if odt else torch.bfloat16, device="cuda")
+    if w.varlen:
+        lse = torch.empty((w.H, w.total_tokens), dtype=torch.float32, device="cuda")
+    else:
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device="cuda")
+    opts = fa.fa_fwd_opts_default()
+    opts.o_dtype = odt
+    opts.rescale_threshold = args.tau
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = fa.fa_fwd_ex(q, k, v, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(w.causal),
+                          off, stream, opts)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(w.name)
+    result = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak (d=128, N=4096 causal)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 Q/K/V",
+        "config": {**w.describe(), "rescale_threshold": args.tau,
+                   "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "avg_launch_ms": round(avg_launch_ms, 5),
+                     "algorithmic_hbm_bytes": w.io_bytes()},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

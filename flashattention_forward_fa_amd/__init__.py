@@ -1,6 +1,169 @@
 """MI355X-native FlashAttention forward: Python binding over the C-ABI library libfa.
 
 The binding only marshals arguments; every step of the attention forward runs
-in the HIP kernels of ``libfa.so``.  The library is loaded on first use and a
-missing or unloadable library raises -- there is no CPU fallback.
+in the HIP kernels of ``libfa.so`` (built in-tree by ``build.py``).  The
+library is loaded on first use; a missing or unloadable library raises -- there
+is no CPU fallback.
+
+Entry points mirror ``include/fa.h``: ``fa_fwd``, ``fa_fwd_ex``,
+``fa_fwd_check``, ``fa_status_string``, ``fa_fwd_opts_default``,
+``fa_version``.  Pointer arguments accept torch tensors (their data pointer) or
+integers; ``stream`` accepts a ``torch.cuda.Stream``, an integer hipStream_t or
+None (torch's current stream).  ``attention`` is a convenience wrapper that
+allocates O and LSE with torch and raises on a non-zero status.
 """
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
+           "FA_DTYPE_BF16", "FA_DTYPE_F32", "FA_SCHEDULE_AUTO", "FA_SCHEDULE_LINEAR",
+           "FA_SCHEDULE_LPT", "FaFwdOpts", "FaError", "library_path", "load", "fa_fwd",
+           "fa_fwd_ex", "fa_fwd_check", "fa_status_string", "fa_fwd_opts_default",
+           "fa_version", "attention"]
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
+FA_SCHEDULE_AUTO, FA_SCHEDULE_LINEAR, FA_SCHEDULE_LPT = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str = "fa_fwd"):
+        super().__init__(f"{what} returned {status} ({fa_status_string(status)})")
+        self.status = status
+
+
+class FaFwdOpts(ctypes.Structure):
+    """Mirror of ``fa_fwd_opts`` in include/fa.h."""
+    _fields_ = [("o_dtype", ctypes.c_int32), ("rescale_threshold", ctypes.c_float),
+                ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+def load():
+    """Load libfa.so (once).  Raises if it is missing: build it with build.py."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libfa.so not found at {path}; build it with "
+                           f"`python -m flashattention_forward_fa_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    common = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.argtypes = common + [vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_ex.argtypes = common + [vp, ctypes.POINTER(FaFwdOpts)]
+    lib.fa_fwd_ex.restype = i
+    lib.fa_fwd_check.argtypes = common + [ctypes.POINTER(FaFwdOpts)]
+    lib.fa_fwd_check.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_fwd_opts_default.argtypes = [ctypes.POINTER(FaFwdOpts)]
+    lib.fa_fwd_opts_default.restype = None
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def fa_fwd_opts_default() -> FaFwdOpts:
+    opts = FaFwdOpts()
+    load().fa_fwd_opts_default(ctypes.byref(opts))
+    return opts
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets=None,
+           stream=None) -> int:
+    return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                         float(scale), int(causal), _ptr(varlen_offsets), _stream(stream))
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets=None,
+              stream=None, opts: FaFwdOpts | None = None) -> int:
+    return load().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                            float(scale), int(causal), _ptr(varlen_offsets), _stream(stream),
+                            ctypes.byref(opts) if opts is not None else None)
+
+
+def fa_fwd_check(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets=None,
+                 opts: FaFwdOpts | None = None) -> int:
+    return load().fa_fwd_check(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk,
+                               d, float(scale), int(causal), _ptr(varlen_offsets),
+                               ctypes.byref(opts) if opts is not None else None)
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> int:
+    return load().fa_version()
+
+
+def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_seqlen=None,
+              o_dtype=FA_DTYPE_BF16, rescale_threshold: float = 8.0,
+              schedule: int = FA_SCHEDULE_AUTO, stream=None):
+    """Allocate O and LSE with torch on q's device and run fa_fwd_ex.
+
+    Fixed length: q [B,Nq,H,d], k/v [B,Nk,H,d] bf16 -> o [B,Nq,H,d], lse [B,H,Nq].
+    Varlen: q/k/v [T,H,d] and int32 offsets [B+1] on the device, max_seqlen =
+    the longest sequence -> o [T,H,d], lse [H,T].
+    """
+    import torch
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, k, v must be bfloat16")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    odt = torch.float32 if o_dtype == FA_DTYPE_F32 else torch.bfloat16
+    o = torch.empty(q.shape, dtype=odt, device=q.device)
+    if varlen_offsets is None:
+        B, Nq, H, d = q.shape
+        Nk = k.shape[1]
+        if k.shape != (B, Nk, H, d) or v.shape != k.shape:
+            raise ValueError("k, v must be [B, Nk, H, d] matching q")
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    else:
+        T, H, d = q.shape
+        if k.shape != q.shape or v.shape != q.shape:
+            raise ValueError("packed q, k, v must have the same shape")
+        if varlen_offsets.dtype != torch.int32:
+            raise TypeError("varlen offsets must be int32")
+        B = varlen_offsets.numel() - 1
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with varlen offsets")
+        Nq = Nk = int(max_seqlen)
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    opts = fa_fwd_opts_default()
+    opts.o_dtype = o_dtype
+    opts.rescale_threshold = rescale_threshold
+    opts.schedule = schedule
+    st = fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets, stream, opts)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_ex")
+    return o, lse

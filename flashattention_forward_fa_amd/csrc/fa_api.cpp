@@ -1,0 +1,129 @@
+// fa_api.cpp -- the C ABI of libfa: argument checks, tile-count set-up, launch.
+//
+// Every argument check runs before the first HIP call, so a rejected call
+// enqueues nothing and fa_fwd_check can run on a machine without a GPU.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kVersion = 100;   // 0.1.0
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int check_args(const void *q, const void *k, const void *v, const void *o, const float *lse,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               const int32_t *offsets, const fa_fwd_opts &opts) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!isfinite(opts.rescale_threshold) || opts.rescale_threshold < 0.f ||
+        opts.rescale_threshold > 64.f)
+        return FA_ERR_INVALID_ARG;
+    if (opts.schedule < FA_SCHEDULE_AUTO || opts.schedule > FA_SCHEDULE_LPT) return FA_ERR_INVALID_ARG;
+    if (opts.reserved != 0) return FA_ERR_INVALID_ARG;
+    if (opts.o_dtype != FA_DTYPE_BF16 && opts.o_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (offsets) {
+        if ((uintptr_t)offsets & 3u) return FA_ERR_INVALID_ARG;
+        if (Nq != Nk) return FA_ERR_INVALID_ARG;   // packed sequences attend to themselves
+    }
+    // Tile count and element offsets must fit the kernel's integer arithmetic.
+    const int64_t num_m = ((int64_t)Nq + fa::kBlockM - 1) / fa::kBlockM;
+    if ((int64_t)B * H * num_m >= (int64_t)1 << 31) return FA_ERR_INVALID_ARG;
+    if ((int64_t)H * d >= (int64_t)1 << 31) return FA_ERR_INVALID_ARG;
+    if ((int64_t)B * Nq >= (int64_t)1 << 31 || (int64_t)B * Nk >= (int64_t)1 << 31)
+        return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void fa_fwd_opts_default(fa_fwd_opts *opts) {
+    if (!opts) return;
+    opts->o_dtype = FA_DTYPE_BF16;
+    opts->rescale_threshold = 8.0f;
+    opts->schedule = FA_SCHEDULE_AUTO;
+    opts->reserved = 0;
+}
+
+int fa_fwd_check(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                 const int32_t *varlen_offsets, const fa_fwd_opts *opts) {
+    fa_fwd_opts def;
+    fa_fwd_opts_default(&def);
+    return check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets,
+                      opts ? *opts : def);
+}
+
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              const int32_t *varlen_offsets, void *stream, const fa_fwd_opts *opts) {
+    fa_fwd_opts op;
+    fa_fwd_opts_default(&op);
+    if (opts) op = *opts;
+    const int st = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets, op);
+    if (st != FA_OK) return st;
+
+    fa::FwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.offsets = varlen_offsets;
+    p.B = B;
+    p.H = H;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.num_m = (Nq + fa::kBlockM - 1) / fa::kBlockM;
+    p.num_tiles = B * H * p.num_m;
+    const bool lpt_default = causal != 0;
+    p.lpt = op.schedule == FA_SCHEDULE_LPT ? 1 : op.schedule == FA_SCHEDULE_LINEAR ? 0 : lpt_default;
+    // The kernel tracks the maximum of the unscaled scores, which is the
+    // maximum of the scaled ones only for scale >= 0.  A negative scale is
+    // applied as softmax(|s| * (-Q) K^T): negating bf16 Q is exact.
+    p.negate_q = scale < 0.f ? 1 : 0;
+    p.scale = fabsf(scale);
+    // scale_log2 = |scale| * log2(e), computed in double and rounded once.
+    p.scale_log2 = (float)((double)p.scale * 1.4426950408889634073599246810019);
+    p.threshold = op.rescale_threshold;
+
+    // Clear a stale error so the status below belongs to this launch.
+    (void)hipGetLastError();
+    const int err = fa::launch_fwd(p, d, causal != 0,
+                                   op.o_dtype == FA_DTYPE_F32 ? fa::OutType::F32 : fa::OutType::BF16,
+                                   stream);
+    return err == 0 ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           const int32_t *varlen_offsets, void *stream) {
+    return fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets, stream,
+                     nullptr);
+}
+
+const char *fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_INVALID_ARG: return "invalid argument";
+        case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case FA_ERR_HIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

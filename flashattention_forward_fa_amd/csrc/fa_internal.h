@@ -1,0 +1,38 @@
+// fa_internal.h -- what the C-ABI layer hands to the kernel launcher.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+// Tile shape of the forward kernel: a workgroup of kWaves wavefronts owns
+// kBlockM = 32 * kWaves query rows (32 per wave); K/V stream in blocks of
+// kBlockN keys.
+constexpr int kWaves = 8;
+constexpr int kBlockM = 32 * kWaves;
+constexpr int kBlockN = 64;
+constexpr int kNumXcd = 8;   // MI355X: 8 accelerator complex dies, one L2 each
+
+enum class OutType : int { BF16 = 0, F32 = 1 };
+
+struct FwdParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    float *lse;
+    const int32_t *offsets;   // varlen: int32 [B+1]; nullptr for fixed length
+    int B, H, Nq, Nk;         // varlen: Nq = Nk = upper bound of the lengths
+    int num_m;                // query tiles per (batch, head) (upper bound for varlen)
+    int num_tiles;            // grid size
+    int lpt;                  // 1: longest-first order
+    int negate_q;             // 1 when the caller's scale was negative (see launch set-up)
+    float scale;              // |s|
+    float scale_log2;         // |s| * log2(e), rounded once from double
+    float threshold;          // tau
+};
+
+// Enqueue the forward kernel; returns a hipError_t value (0 = success).
+int launch_fwd(const FwdParams &p, int d, bool causal, OutType out, void *stream);
+
+}  // namespace fa

@@ -1,0 +1,133 @@
+/*
+ * fa.h -- C ABI of libfa, a FlashAttention forward pass for AMD MI355X (gfx950).
+ *
+ * Operation (one call):
+ *
+ *     O   = softmax(scale * Q K^T) V        row-wise softmax over the keys
+ *     LSE = ln sum_j exp(scale * q_i . k_j)  natural-log log-sum-exp per row
+ *
+ * as defined on "Flash Attention 4" (mlc.ai), section "algorithm structure"
+ * (O_i = o_i / l_i with the online row state r_i, l_i, o_i) and on
+ * "FlashAttention：一次前向计算" (qingsen), sections "what attention computes"
+ * and "general update" (explicit scale s, L_i = s m_i + log l_i).  K/V are
+ * visited block by block with the online-softmax row state; the score matrix
+ * never reaches memory.  The exponent is base 2 with the scale folded in
+ * (scale_log2 = scale * log2 e), and the reference of a row is only moved when
+ * the new block maximum exceeds it by more than the rescale threshold tau
+ * (FA4 page, "algorithm structure": keep the old reference while
+ * delta >= -tau; tau = 8 by default, tau = 0 rescales whenever the maximum
+ * grows).
+ *
+ * Causal masking is aligned to the bottom-right corner (FA4 page, section
+ * "Causal Mask"): query i may use keys j <= i + Nk - Nq.  A row with no usable
+ * key gets O = 0 and LSE = -inf.
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, o, lse and varlen_offsets are DEVICE pointers on the current
+ *     HIP device; the caller owns them; libfa keeps no pointer after return.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  A return of FA_OK means the kernel was enqueued.
+ *   - Arguments are checked before any HIP call; a bad argument returns an
+ *     error status and enqueues nothing.  No call aborts or prints.
+ *   - Inputs are bf16 (raw 16-bit patterns).  O is bf16 by default (fp32 via
+ *     fa_fwd_ex); LSE is fp32.
+ *
+ * Layouts (row-major, contiguous, head dimension fastest):
+ *   fixed length (varlen_offsets == NULL):
+ *     q [B, Nq, H, d], k and v [B, Nk, H, d], o [B, Nq, H, d], lse [B, H, Nq]
+ *   packed variable length (varlen_offsets != NULL):
+ *     varlen_offsets: int32 [B + 1], offsets[0] = 0, non-decreasing; sequence
+ *     b holds tokens offsets[b] .. offsets[b+1]-1 and attends to itself
+ *     (self attention, Nq = Nk = its length).  With T = offsets[B]:
+ *     q, k, v, o [T, H, d], lse [H, T].  Nq and Nk must both equal an upper
+ *     bound of every sequence length (normally the maximum).  The device reads
+ *     the offsets; they are not validated -- offsets that decrease, exceed T
+ *     or a length above Nq are undefined behaviour.
+ *
+ * Supported: d in {64, 128}; B, H, Nq, Nk >= 1; any Nq, Nk (tails masked);
+ * pointers 16-byte aligned; B*H*ceil(Nq/256) below 2^31.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, size <= 0, bad option value */
+    FA_ERR_UNSUPPORTED = -2,   /* well-formed but not implemented: d not 64/128, dtype */
+    FA_ERR_HIP = -3            /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/* Element type of O. */
+typedef enum fa_dtype {
+    FA_DTYPE_BF16 = 0,
+    FA_DTYPE_F32 = 1
+} fa_dtype;
+
+/* Tile order. AUTO = longest-first (LPT) for causal or varlen, linear otherwise. */
+typedef enum fa_schedule {
+    FA_SCHEDULE_AUTO = 0,
+    FA_SCHEDULE_LINEAR = 1,
+    FA_SCHEDULE_LPT = 2
+} fa_schedule;
+
+/*
+ * Options of fa_fwd_ex.
+ *   o_dtype           : fa_dtype of O (default FA_DTYPE_BF16).
+ *   rescale_threshold : tau in base-2 exponent units, finite, 0 <= tau <= 64
+ *                       (default 8).  0 = always rescale when the row maximum
+ *                       grows.  The upper bound keeps P <= 2^tau and the row
+ *                       sum finite in fp32.
+ *   schedule          : fa_schedule (default FA_SCHEDULE_AUTO).
+ *   reserved          : must be 0.
+ */
+typedef struct fa_fwd_opts {
+    int32_t o_dtype;
+    float rescale_threshold;
+    int32_t schedule;
+    int32_t reserved;
+} fa_fwd_opts;
+
+/* Fill *opts with the defaults (bf16 O, tau = 8, automatic schedule). */
+void fa_fwd_opts_default(fa_fwd_opts *opts);
+
+/*
+ * Attention forward with the default options.  scale is explicit (there is
+ * no default; 1/sqrt(d) is the usual choice); it may be any finite value.
+ * causal: 0 = full attention, 1 = bottom-right causal mask.
+ * Returns a fa_status.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           const int32_t *varlen_offsets, void *stream);
+
+/* As fa_fwd, with options (opts == NULL means the defaults). */
+int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              const int32_t *varlen_offsets, void *stream, const fa_fwd_opts *opts);
+
+/*
+ * The argument checks of fa_fwd_ex alone: returns the status fa_fwd_ex would
+ * return before launching, and makes no HIP call (usable without a GPU).
+ */
+int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
+                 const float *lse, int B, int H, int Nq, int Nk, int d, float scale,
+                 int causal, const int32_t *varlen_offsets, const fa_fwd_opts *opts);
+
+/* A static, NUL-terminated description of a status code. */
+const char *fa_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

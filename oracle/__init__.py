@@ -79,8 +79,14 @@ class Oracle:
                                              _I64P, ctypes.c_int64, ctypes.c_int64, _I64P,
                                              _F64P, _F64P]
         lib.oracle_attn_fwd_rows.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
+
+    def num_threads(self) -> int:
+        """OpenMP threads the oracle's parallel loops use."""
+        return int(self.lib.oracle_num_threads())
 
     def attention(self, q, k, v, scale: float, causal: bool):
         """Fixed length: q [B,Nq,H,d], k/v [B,Nk,H,d] -> (o [B,Nq,H,d], lse [B,H,Nq])."""

@@ -42,6 +42,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads an OpenMP region of this library uses (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Number of keys query i may use. */
 static int64_t valid_keys(int64_t i, int64_t Nq, int64_t Nk, int causal)

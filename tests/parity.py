@@ -1,0 +1,143 @@
+"""Helpers shared by the GPU parity tests: upload a workload, run the HIP path
+through the C ABI, and compare with the oracle at the stated tolerances.
+
+Tolerances (O compared widened to fp64 against the unrounded fp64 oracle):
+  * max |O - O_ref| <= 1e-2 and mean |O - O_ref| <= 1e-3.
+  * When O is stored in bf16, one output element in [4, 8) can carry a
+    rounding error of half a bf16 ulp = 2^-6 ~ 0.0156 > 1e-2 no matter how the
+    value was computed.  For such elements the bound is half an ulp of the
+    reference value plus 1e-3; every element below 4 in magnitude keeps the
+    plain 1e-2 bound, and the fp32-output runs keep 1e-2 everywhere.
+  * LSE: |LSE - LSE_ref| <= 1e-3 * max(1, |LSE_ref|) (a relative bound with a
+    floor, since short causal rows can have LSE near 0); -inf must match -inf.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from flashattention_forward_fa_amd import workloads as wl
+
+O_MAX_ABS = 1e-2
+O_MEAN_ABS = 1e-3
+LSE_REL = 1e-3
+
+
+def to_device(w):
+    import torch
+    dev = "cuda"
+    q = torch.from_numpy(w.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    k = torch.from_numpy(w.k.view(np.int16)).view(torch.bfloat16).to(dev)
+    v = torch.from_numpy(w.v.view(np.int16)).view(torch.bfloat16).to(dev)
+    off = None
+    if w.varlen:
+        off = torch.from_numpy(np.ascontiguousarray(w.offsets.astype(np.int32))).to(dev)
+    return q, k, v, off
+
+
+def run_gpu(w, *, tau=8.0, o_dtype=None, schedule=0, tensors=None):
+    """Run the HIP path on workload w; returns (o float64 numpy, lse float64 numpy)."""
+    import torch
+    import flashattention_forward_fa_amd as fa
+    q, k, v, off = tensors if tensors is not None else to_device(w)
+    if o_dtype is None:
+        o_dtype = fa.FA_DTYPE_F32 if w.o_dtype == "f32" else fa.FA_DTYPE_BF16
+    o, lse = fa.attention(q, k, v, w.scale, w.causal, varlen_offsets=off,
+                          max_seqlen=w.Nq if w.varlen else None, o_dtype=o_dtype,
+                          rescale_threshold=tau, schedule=schedule)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def inputs_f64(w):
+    return wl.bf16_to_f64(w.q), wl.bf16_to_f64(w.k), wl.bf16_to_f64(w.v)
+
+
+def half_ulp_bf16(x):
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+def o_bound(o_ref, bf16_out: bool):
+    if not bf16_out:
+        return np.full(np.shape(o_ref), O_MAX_ABS)
+    return np.maximum(O_MAX_ABS, half_ulp_bf16(o_ref) + 1e-3)
+
+
+def compare(o, lse, o_ref, lse_ref, *, bf16_out: bool, what: str = ""):
+    """Assert the tolerances; returns a dict of error statistics."""
+    o = np.asarray(o, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    assert o.shape == o_ref.shape, f"{what}: O shape {o.shape} vs {o_ref.shape}"
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    err = np.abs(o - o_ref)
+    bound = o_bound(o_ref, bf16_out)
+    bad = err > bound
+    stats = dict(o_max_abs=float(err.max(initial=0.0)), o_mean_abs=float(err.mean()) if err.size else 0.0,
+                 n_over_1e2=int(np.count_nonzero(err > O_MAX_ABS)))
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, err - bound, -np.inf)), err.shape)
+        raise AssertionError(f"{what}: O error {err[idx]:.3e} > bound {bound[idx]:.3e} at {idx} "
+                             f"(ref {o_ref[idx]:.5f}, got {o[idx]:.5f}); {int(bad.sum())} elements")
+    assert stats["o_mean_abs"] <= O_MEAN_ABS, f"{what}: mean |dO| {stats['o_mean_abs']:.3e}"
+
+    lse = np.asarray(lse, dtype=np.float64)
+    lse_ref = np.asarray(lse_ref, dtype=np.float64)
+    assert lse.shape == lse_ref.shape, f"{what}: LSE shape {lse.shape} vs {lse_ref.shape}"
+    ninf_ref = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), ninf_ref), f"{what}: -inf pattern of LSE differs"
+    fin = ~ninf_ref
+    assert np.all(np.isfinite(lse[fin])), f"{what}: non-finite LSE"
+    dl = np.abs(lse[fin] - lse_ref[fin])
+    lb = LSE_REL * np.maximum(1.0, np.abs(lse_ref[fin]))
+    if dl.size:
+        stats["lse_max_abs"] = float(dl.max())
+        stats["lse_max_rel"] = float((dl / np.maximum(np.abs(lse_ref[fin]), 1e-30)).max())
+        if np.any(dl > lb):
+            j = int(np.argmax(dl - lb))
+            raise AssertionError(f"{what}: LSE error {dl[j]:.3e} > {lb[j]:.3e} (ref {lse_ref[fin][j]})")
+    return stats
+
+
+def sample_rows(w, n_random: int, seed: int = 0):
+    """(b, h, i) triples: tile and block edges, first and last rows, plus random rows."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    if w.varlen:
+        for b, L in enumerate(w.lengths):
+            L = int(L)
+            for i in sorted({0, 1, 2, 31, 32, 63, 64, 255, 256, L // 2, L - 2, L - 1}):
+                if 0 <= i < L:
+                    rows.append((b, int(rng.integers(w.H)), i))
+        for _ in range(n_random):
+            b = int(rng.integers(len(w.lengths)))
+            rows.append((b, int(rng.integers(w.H)), int(rng.integers(int(w.lengths[b])))))
+    else:
+        edges = sorted({0, 1, 2, 31, 32, 63, 64, 127, 128, 255, 256, 257, w.Nq // 2,
+                        w.Nq - 2, w.Nq - 1})
+        for b in range(w.B):
+            for h in (0, w.H - 1):
+                for i in edges:
+                    if 0 <= i < w.Nq:
+                        rows.append((b, h, i))
+        for _ in range(n_random):
+            rows.append((int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.Nq))))
+    return np.array(sorted(set(rows)), dtype=np.int64)
+
+
+def gather_rows(w, o, lse, rows):
+    """Pick the sampled rows out of full GPU outputs."""
+    if w.varlen:
+        t = w.offsets[rows[:, 0]].astype(np.int64) + rows[:, 2]
+        return o[t, rows[:, 1]], lse[rows[:, 1], t]
+    return o[rows[:, 0], rows[:, 2], rows[:, 1]], lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+
+
+def flops_str(w):
+    return f"{w.flops() / 1e9:.2f} GFLOP"
+
+
+def ln(x):
+    return math.log(x)

@@ -1,0 +1,113 @@
+"""The C-ABI library: it loads, exports every function include/fa.h declares,
+and its argument checks return the documented status codes (no GPU: the checks
+run before any HIP call)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import flashattention_forward_fa_amd as fa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
+P = 1 << 20          # a 16-byte aligned stand-in address; the checks never dereference it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = ctypes.CDLL(fa.library_path())
+    names = declared_functions()
+    assert {"fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_status_string",
+            "fa_fwd_opts_default", "fa_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_defaults():
+    assert fa.fa_version() >= 100
+    o = fa.fa_fwd_opts_default()
+    assert (o.o_dtype, o.rescale_threshold, o.schedule, o.reserved) == (0, 8.0, 0, 0)
+
+
+def test_status_strings():
+    assert fa.fa_status_string(fa.FA_OK) == "ok"
+    assert "invalid" in fa.fa_status_string(fa.FA_ERR_INVALID_ARG)
+    assert "unsupported" in fa.fa_status_string(fa.FA_ERR_UNSUPPORTED)
+    assert "HIP" in fa.fa_status_string(fa.FA_ERR_HIP)
+    assert fa.fa_status_string(12345) == "unknown status"
+
+
+def check(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, Nq=100, Nk=100, d=128, scale=0.1, causal=1,
+             varlen_offsets=None, opts=None)
+    a.update(kw)
+    return fa.fa_fwd_check(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                           a["Nk"], a["d"], a["scale"], a["causal"], a["varlen_offsets"], a["opts"])
+
+
+def opts(**kw):
+    o = fa.fa_fwd_opts_default()
+    for key, val in kw.items():
+        setattr(o, key, val)
+    return o
+
+
+def test_valid_arguments():
+    assert check() == fa.FA_OK
+    assert check(d=64, causal=0) == fa.FA_OK
+    assert check(varlen_offsets=P, Nq=8192, Nk=8192) == fa.FA_OK
+    assert check(scale=-0.5) == fa.FA_OK and check(scale=0.0) == fa.FA_OK
+    assert check(opts=opts(o_dtype=fa.FA_DTYPE_F32, rescale_threshold=0.0,
+                           schedule=fa.FA_SCHEDULE_LPT)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_null_and_misaligned_pointers(field):
+    assert check(**{field: None}) == fa.FA_ERR_INVALID_ARG
+    assert check(**{field: P + 8}) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("Nq", 0), ("Nk", -3), ("d", 0),
+                                         ("causal", 2), ("scale", math.inf),
+                                         ("scale", math.nan)])
+def test_bad_sizes(field, value):
+    assert check(**{field: value}) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [32, 80, 96, 192, 256])
+def test_unsupported_head_dim(d):
+    assert check(d=d) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("tau", [-1.0, 64.5, math.inf, math.nan])
+def test_bad_threshold(tau):
+    assert check(opts=opts(rescale_threshold=tau)) == fa.FA_ERR_INVALID_ARG
+
+
+def test_bad_options():
+    assert check(opts=opts(o_dtype=7)) == fa.FA_ERR_UNSUPPORTED
+    assert check(opts=opts(schedule=3)) == fa.FA_ERR_INVALID_ARG
+    assert check(opts=opts(reserved=1)) == fa.FA_ERR_INVALID_ARG
+
+
+def test_varlen_rules():
+    assert check(varlen_offsets=P, Nq=100, Nk=200) == fa.FA_ERR_INVALID_ARG
+    assert check(varlen_offsets=P + 2, Nq=100, Nk=100) == fa.FA_ERR_INVALID_ARG
+
+
+def test_size_overflow_rejected():
+    assert check(B=1 << 20, H=1 << 10, Nq=1 << 16, Nk=16) == fa.FA_ERR_INVALID_ARG
+
+
+def test_rejected_launch_makes_no_hip_call():
+    """fa_fwd with a bad argument returns before touching HIP (safe without a GPU)."""
+    st = fa.fa_fwd(None, P, P, P, P, 1, 1, 16, 16, 128, 0.1, 0, None, stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG
+    st = fa.fa_fwd(P, P, P, P, P, 1, 1, 16, 16, 96, 0.1, 0, None, stream=0)
+    assert st == fa.FA_ERR_UNSUPPORTED

@@ -1,0 +1,221 @@
+"""HIP path vs the fp64 oracle, through the C ABI, element by element.
+
+Small problems (several tiles, ragged tails, edge cases) are compared in full;
+the five measured configurations run at their full sizes in the launch
+configuration the benchmark times and are compared on sampled rows (tile and
+block edges, first/last rows, random rows) that the oracle computes one by one.
+Both the conditional rescale (tau = 8) and the always-rescale variant (tau = 0)
+must pass.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from flashattention_forward_fa_amd import workloads as wl
+from tests import parity
+from tests.oracle_pins import load_worked_example
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import flashattention_forward_fa_amd as fa
+    fa.load()   # raises if libfa.so is missing: there is no fallback
+
+
+def _full_check(w, tau, o_dtype=None, what=""):
+    o, lse = parity.run_gpu(w, tau=tau, o_dtype=o_dtype)
+    q, k, v = parity.inputs_f64(w)
+    if w.varlen:
+        o_ref, lse_ref = oracle.attention_varlen(q, k, v, w.offsets, w.scale, w.causal)
+    else:
+        o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
+    bf16_out = (o_dtype == 0) if o_dtype is not None else (w.o_dtype == "bf16")
+    return parity.compare(o, lse, o_ref, lse_ref, bf16_out=bf16_out, what=what or w.name)
+
+
+# ------------------------------------------------------------ worked example
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("o_dtype", [0, 1])
+def test_worked_example_padded(causal, o_dtype):
+    """The page's 2-query / 4-key example with s = ln 2, zero-padded to d = 64 (exact in bf16).
+
+    Non-causal: O = [[7/8, 3/4], [4/3, 1/3]], LSE = (ln 8, ln 9) as printed.
+    Causal, bottom-right (Nq = 2, Nk = 4): O = [[5/7, 6/7], [4/3, 1/3]], LSE = (ln 7, ln 9).
+    """
+    import torch
+    import flashattention_forward_fa_amd as fa
+    g = load_worked_example()
+    d = 64
+    pad = lambda x: np.pad(x, ((0, 0), (0, d - x.shape[1])))
+    mk = lambda x: torch.from_numpy(wl.bf16_bits(pad(x)[None, :, None, :].astype(np.float32))
+                                    .view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = mk(g["Q"]), mk(g["K"]), mk(g["V"])
+    for tau in (8.0, 0.0):
+        o, lse = fa.attention(q, k, v, math.log(2.0), causal, o_dtype=o_dtype, rescale_threshold=tau)
+        torch.cuda.synchronize()
+        o = o.double().cpu().numpy()[0, :, 0, :2]
+        lse = lse.double().cpu().numpy()[0, 0]
+        if causal:
+            want_o = [[5 / 7, 6 / 7], [4 / 3, 1 / 3]]
+            want_l = [math.log(7), math.log(9)]
+        else:
+            want_o = [[7 / 8, 3 / 4], [4 / 3, 1 / 3]]
+            want_l = [math.log(8), math.log(9)]
+        tol = 1e-5 if o_dtype == 1 else 4e-3
+        np.testing.assert_allclose(o, want_o, atol=tol)
+        np.testing.assert_allclose(lse, want_l, atol=1e-5)
+
+
+# ------------------------------------------------------------ small, full compare
+
+SMALL = [
+    # B, H, Nq, Nk, d, causal
+    (2, 3, 300, 300, 64, False),
+    (2, 3, 300, 300, 64, True),
+    (1, 4, 300, 300, 128, False),
+    (1, 4, 300, 300, 128, True),
+    (1, 2, 100, 700, 128, True),     # Nq < Nk: bottom-right alignment
+    (1, 2, 100, 700, 64, False),
+    (1, 2, 700, 100, 128, True),     # Nq > Nk: leading rows have no key
+    (2, 1, 1, 1, 64, True),
+    (1, 3, 1, 1000, 128, True),
+    (1, 2, 257, 513, 128, False),    # one past a tile / block boundary
+    (3, 5, 64, 64, 128, True),
+    (1, 8, 512, 512, 64, True),      # B*H a multiple of 8: XCD-aware order
+]
+
+
+@pytest.mark.parametrize("tau", [8.0, 0.0])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}q{}k{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_small_full(shape, tau):
+    B, H, Nq, Nk, d, causal = shape
+    w = wl.make_fixed(B, H, Nq, Nk, d, seed=B * 1000 + Nq + Nk + d, causal=causal)
+    _full_check(w, tau)
+    _full_check(w, tau, o_dtype=1, what=w.name + "/f32out")
+
+
+@pytest.mark.parametrize("tau", [8.0, 0.0])
+def test_small_outliers_force_rescale(tau):
+    """K rows scaled by 8 (the long-sequence recipe) at a size the oracle finishes in full."""
+    w = wl.make_fixed(1, 4, 1000, 1000, 128, seed=77, causal=True, outlier_frac=0.01)
+    _full_check(w, tau)
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.7])
+def test_scale_values(scale):
+    """Negative, zero and large scales (scale 0: O is the mean of the valid V rows)."""
+    w = wl.make_fixed(1, 2, 200, 300, 64, seed=5, causal=True, scale=scale)
+    _full_check(w, 8.0, o_dtype=1)
+
+
+def test_small_varlen_full():
+    w = wl.make_varlen(3, 64, seed=31, nseq=5, len_lo=1, len_hi=700)
+    _full_check(w, 8.0)
+    _full_check(w, 0.0)
+    w128 = wl.make_varlen(2, 128, seed=32, lengths=[300, 1, 256, 257, 40], causal=True)
+    _full_check(w128, 8.0, o_dtype=1)
+    wnc = wl.make_varlen(2, 64, seed=33, lengths=[17, 600, 129], causal=False)
+    _full_check(wnc, 8.0)
+
+
+def test_varlen_equals_separate_calls():
+    """A packed call gives, bit for bit, what fixed-length calls on each sequence give."""
+    w = wl.make_varlen(4, 128, seed=41, lengths=[513, 70, 256, 1000], causal=True)
+    o, lse = parity.run_gpu(w)
+    for b, L in enumerate(w.lengths):
+        sl = slice(int(w.offsets[b]), int(w.offsets[b + 1]))
+        one = wl.Workload("seq", 1, w.H, int(L), int(L), w.d, True, w.scale, "bf16", 0,
+                          w.q[sl][None], w.k[sl][None], w.v[sl][None])
+        o1, l1 = parity.run_gpu(one)
+        assert np.array_equal(o[sl], o1[0]), f"sequence {b}"
+        assert np.array_equal(lse[:, sl], l1[0]), f"sequence {b} lse"
+
+
+def test_schedules_agree_bitwise():
+    """Tile order changes which workgroup computes a tile, never its arithmetic."""
+    w = wl.make_fixed(2, 8, 600, 600, 128, seed=3, causal=True)
+    t = parity.to_device(w)
+    ref = parity.run_gpu(w, schedule=0, tensors=t)
+    for sch in (1, 2):
+        got = parity.run_gpu(w, schedule=sch, tensors=t)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), sch
+    wv = wl.make_varlen(3, 64, seed=4, lengths=[900, 10, 300, 513], causal=True)
+    tv = parity.to_device(wv)
+    ref = parity.run_gpu(wv, schedule=2, tensors=tv)
+    got = parity.run_gpu(wv, schedule=1, tensors=tv)
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def test_outputs_stay_in_bounds():
+    """Canary words around O and LSE are untouched (the kernel writes only its rows)."""
+    import torch
+    import flashattention_forward_fa_amd as fa
+    w = wl.make_fixed(1, 3, 333, 333, 64, seed=9, causal=True)
+    q, k, v, _ = parity.to_device(w)
+    n_o = q.numel()
+    pad = 256
+    o_buf = torch.full((n_o + 2 * pad,), -12345.0, dtype=torch.float32, device="cuda")
+    l_buf = torch.full((w.H * w.Nq + 2 * pad,), -777.0, dtype=torch.float32, device="cuda")
+    o = o_buf[pad:pad + n_o]
+    lse = l_buf[pad:pad + w.H * w.Nq]
+    opts = fa.fa_fwd_opts_default()
+    opts.o_dtype = fa.FA_DTYPE_F32
+    st = fa.fa_fwd_ex(q, k, v, o, lse, 1, w.H, w.Nq, w.Nk, w.d, w.scale, 1, None, None, opts)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    ob = o_buf.cpu().numpy()
+    lb = l_buf.cpu().numpy()
+    assert np.all(ob[:pad] == -12345.0) and np.all(ob[pad + n_o:] == -12345.0)
+    assert np.all(lb[:pad] == -777.0) and np.all(lb[pad + w.H * w.Nq:] == -777.0)
+    assert np.all(np.isfinite(ob[pad:pad + n_o]))
+
+
+# ------------------------------------------------------------ the five configurations
+
+_cache = {}
+
+
+def _config(n):
+    if n not in _cache:
+        _cache.clear()
+        w = wl.config(n)
+        rows = parity.sample_rows(w, n_random=256, seed=n)
+        q, k, v = parity.inputs_f64(w)
+        o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, w.causal, rows,
+                                               offsets=w.offsets if w.varlen else None)
+        del q, k, v
+        _cache[n] = (w, rows, o_ref, lse_ref, parity.to_device(w))
+    return _cache[n]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tau", [8.0, 0.0])
+def test_config(n, tau):
+    if n == 1:
+        w = wl.config(1)
+        stats = _full_check(w, tau)
+        print(f"config 1 tau={tau}: {stats}")
+        return
+    w, rows, o_ref, lse_ref, t = _config(n)
+    o, lse = parity.run_gpu(w, tau=tau, tensors=t)
+    assert np.all(np.isfinite(o)), "non-finite O"
+    go, gl = parity.gather_rows(w, o, lse, rows)
+    stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=True, what=f"config {n} tau={tau}")
+    print(f"config {n} tau={tau}: {len(rows)} rows {stats}")
+    # properties over every row: LSE finite; causal row 0 is exactly V row 0
+    assert np.all(np.isfinite(lse))
+    if w.causal:
+        v0 = wl.bf16_to_f64(w.v)
+        if w.varlen:
+            first = w.offsets[:-1].astype(np.int64)
+            assert np.array_equal(o[first], v0[first])
+        else:
+            assert np.array_equal(o[:, 0], v0[:, 0])
