@@ -91,12 +91,20 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
     const bool lpt_default = causal != 0;
     p.lpt = op.schedule == FA_SCHEDULE_LPT ? 1 : op.schedule == FA_SCHEDULE_LINEAR ? 0 : lpt_default;
     // The kernel tracks the maximum of the unscaled scores, which is the
-    // maximum of the scaled ones only for scale >= 0.  A negative scale is
-    // applied as softmax(|s| * (-Q) K^T): negating bf16 Q is exact.
-    p.negate_q = scale < 0.f ? 1 : 0;
+    // maximum of the scaled ones only for scale > 0.  A negative scale is
+    // applied as softmax(|s| * (-Q) K^T) (negating bf16 Q is exact); scale 0
+    // as softmax(1 * 0 K^T), which keeps masked scores at -inf instead of
+    // -inf * 0.
+    p.q_xor = 0u;
+    p.q_and = 0xFFFFFFFFu;
+    if (scale < 0.f) p.q_xor = 0x80008000u;
     p.scale = fabsf(scale);
     // scale_log2 = |scale| * log2(e), computed in double and rounded once.
     p.scale_log2 = (float)((double)p.scale * 1.4426950408889634073599246810019);
+    if (scale == 0.f) {
+        p.q_and = 0u;
+        p.scale_log2 = 1.0f;
+    }
     p.threshold = op.rescale_threshold;
 
     // Clear a stale error so the status below belongs to this launch.

@@ -17,7 +17,8 @@
 //
 // and finally O = o / l (0 when l = 0) and LSE = ln l + r * scale ("Flash
 // Attention 4", section "rescale and write-back": valid for any consistent
-// reference).  The first block of a row starts from r = -inf, so delta = -inf
+// reference).  O is normalised by the row sum of the bf16-rounded P that the
+// PV product used, LSE by the fp32 row sum (see the softmax step).  The first block of a row starts from r = -inf, so delta = -inf
 // switches to the candidate with alpha = 0 on a zero state, which is the
 // page's first-block case (taken without evaluating delta, which would be
 // -inf * 0 for scale 0).  A candidate of -inf (every key so far masked) keeps
@@ -61,6 +62,7 @@ namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -107,11 +109,16 @@ __device__ __forceinline__ int vt_pos16(int kappa) {
     return ((kappa >> 2) & 1) * 8 + (kappa & 3) + ((kappa >> 3) << 2);
 }
 
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-    __bf16 x = (__bf16)a;   // round to nearest even
-    __bf16 y = (__bf16)b;
-    return (unsigned)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+    const f32x2 f = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+// Sum of the two bf16 halves of a word, accumulated in fp32 (v_dot2 with (1, 1)).
+__device__ __forceinline__ float add_bf16x2(unsigned word, float acc) {
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc, false);
 }
 
 // ------------------------------------------------------------------ scheduler
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     for (int ds = 0; ds < T::NDS; ++ds) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (row_ok) x = *(const u32x4 *)(Qg + (int64_t)qrow * tok + 16 * ds + 8 * g);
-        if (p.negate_q) x ^= 0x80008000u;   // flip the sign of every bf16
+        x = (x ^ p.q_xor) & p.q_and;        // sign flip (scale < 0) or zero (scale = 0)
         qf[ds] = __builtin_bit_cast(bf16x8, x);
     }
 
@@ -260,7 +267,8 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
 
     float r = -INFINITY;     // exponent reference (unscaled score units)
-    float lsum = 0.f;        // this lane's half of the row sum
+    float lsum = 0.f;        // this lane's half of the row sum of bf16(P) (normalises O)
+    float lsum32 = 0.f;      // ... of the fp32 P (gives LSE)
     const float c = p.scale_log2;
     const float tau = p.threshold;
 
@@ -395,31 +403,37 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
             // P = exp2(S*c - r*c), rounded to bf16 for the PV MFMA.  The row
             // sum is taken over the same bf16 values (v_dot2 with (1, 1)), so
             // numerator and denominator see identical weights.
+            float fsum0 = 0.f, fsum1 = 0.f;
 #pragma unroll
             for (int kt = 0; kt < T::NKT; ++kt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s[kt][i] = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, neg_rc));
+                for (int i = 0; i < 16; ++i) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, neg_rc));
+                    s[kt][i] = pv;
+                    if (i & 1) fsum1 += pv; else fsum0 += pv;
+                }
 
-            const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+            // (Words are kept in scalars: a bit cast of a vector element
+            // reads element 0 in this compiler.)
             float bsum0 = 0.f, bsum1 = 0.f;
             bf16x8 pf[T::NKS];
 #pragma unroll
             for (int ks = 0; ks < T::NKS; ++ks) {
                 const f32x16 &src = s[ks >> 1];
                 const int i0 = 8 * (ks & 1);
-                u32x4 x;
-                x[0] = pack_bf16x2(src[i0 + 0], src[i0 + 1]);
-                x[1] = pack_bf16x2(src[i0 + 2], src[i0 + 3]);
-                x[2] = pack_bf16x2(src[i0 + 4], src[i0 + 5]);
-                x[3] = pack_bf16x2(src[i0 + 6], src[i0 + 7]);
-                bsum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[0]), ones, bsum0, false);
-                bsum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[1]), ones, bsum1, false);
-                bsum0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[2]), ones, bsum0, false);
-                bsum1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[3]), ones, bsum1, false);
+                const unsigned w0 = pack_bf16x2(src[i0 + 0], src[i0 + 1]);
+                const unsigned w1 = pack_bf16x2(src[i0 + 2], src[i0 + 3]);
+                const unsigned w2 = pack_bf16x2(src[i0 + 4], src[i0 + 5]);
+                const unsigned w3 = pack_bf16x2(src[i0 + 6], src[i0 + 7]);
+                bsum0 = add_bf16x2(w0, bsum0);
+                bsum1 = add_bf16x2(w1, bsum1);
+                bsum0 = add_bf16x2(w2, bsum0);
+                bsum1 = add_bf16x2(w3, bsum1);
+                const u32x4 x = {w0, w1, w2, w3};
                 pf[ks] = __builtin_bit_cast(bf16x8, x);
             }
             lsum = lsum * alpha + (bsum0 + bsum1);
+            lsum32 = lsum32 * alpha + (fsum0 + fsum1);
 
             // Conditional rescale of the accumulator, skipped per wave when no
             // row of the wave moved its reference.
@@ -447,6 +461,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
 
     // Epilogue: O = o / l, LSE = ln l + r * scale.
     const float l = lane_pair_sum(lsum);
+    const float l32 = lane_pair_sum(lsum32);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (row_ok) {
         OutT *Og = (OutT *)p.o + ((int64_t)tc.q_tok0 + qrow) * tok + tc.h * D;
@@ -466,7 +481,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
                 }
             }
         if (g == 0) {
-            const float lse = l > 0.f ? logf(l) + r * p.scale : -INFINITY;
+            const float lse = l32 > 0.f ? logf(l32) + r * p.scale : -INFINITY;
             int64_t idx;
             if (VARLEN) idx = (int64_t)tc.h * p.offsets[p.B] + tc.q_tok0 + qrow;
             else        idx = ((int64_t)tc.b * p.H + tc.h) * Nq + qrow;

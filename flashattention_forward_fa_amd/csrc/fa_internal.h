@@ -26,9 +26,10 @@ struct FwdParams {
     int num_m;                // query tiles per (batch, head) (upper bound for varlen)
     int num_tiles;            // grid size
     int lpt;                  // 1: longest-first order
-    int negate_q;             // 1 when the caller's scale was negative (see launch set-up)
-    float scale;              // |s|
-    float scale_log2;         // |s| * log2(e), rounded once from double
+    unsigned q_xor;           // applied to Q's bf16 pairs on load: (q ^ q_xor) & q_and
+    unsigned q_and;
+    float scale;              // |s|, used for LSE
+    float scale_log2;         // exponent scale: |s| * log2(e) rounded once (1 when s = 0)
     float threshold;          // tau
 };
 

@@ -202,14 +202,23 @@ def test_config(n, tau):
     if n == 1:
         w = wl.config(1)
         stats = _full_check(w, tau)
-        print(f"config 1 tau={tau}: {stats}")
+        print(f"config 1 tau={tau} f32 O: {stats}")
+        stats = _full_check(w, tau, o_dtype=0, what=w.name + "/bf16out")
+        print(f"config 1 tau={tau} bf16 O: {stats}")
         return
     w, rows, o_ref, lse_ref, t = _config(n)
+    # fp32 output: the arithmetic against the plain bound
+    o32, lse32 = parity.run_gpu(w, tau=tau, tensors=t, o_dtype=1)
+    go, gl = parity.gather_rows(w, o32, lse32, rows)
+    stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=False, what=f"config {n} tau={tau} f32 O")
+    print(f"config {n} tau={tau} f32 O: {len(rows)} rows {stats}")
+    del o32, lse32
+    # bf16 output: the configuration the benchmark times
     o, lse = parity.run_gpu(w, tau=tau, tensors=t)
     assert np.all(np.isfinite(o)), "non-finite O"
     go, gl = parity.gather_rows(w, o, lse, rows)
     stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=True, what=f"config {n} tau={tau}")
-    print(f"config {n} tau={tau}: {len(rows)} rows {stats}")
+    print(f"config {n} tau={tau} bf16 O: {len(rows)} rows {stats}")
     # properties over every row: LSE finite; causal row 0 is exactly V row 0
     assert np.all(np.isfinite(lse))
     if w.causal:
