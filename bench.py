@@ -106,6 +106,9 @@ def main():
     ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of attention, time a plain device copy of 1 GiB (used to "
+                         "scale the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -120,6 +123,22 @@ def main():
     from tests import parity
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 29                                   # 2^29 bf16 = 1 GiB each way
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n,
+                          "ms_per_copy": round(ms, 4),
+                          "GB_per_s": round(4 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
     fa.load()
     w = wl.config(args.config)
     q, k, v, off = parity.to_device(w)

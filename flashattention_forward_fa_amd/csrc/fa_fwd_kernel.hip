@@ -56,6 +56,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -77,8 +79,7 @@ struct Tile {
     static constexpr int VS = BN + 8;         // V^T row stride in LDS
     static constexpr int K_ELEMS = BN * KS;
     static constexpr int V_ELEMS = D * VS;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static constexpr int LDS_BYTES = (2 * K_ELEMS + 2 * V_ELEMS) * 2;
     static constexpr int NKT = BN / 32;       // 32-key tiles of S^T per block
     static constexpr int NDS = D / 16;        // 16-wide head-dim steps of S^T
     static constexpr int NDT = D / 32;        // 32-wide head-dim tiles of O^T
@@ -216,10 +217,26 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
 }
 
 // ------------------------------------------------------------------ kernel
+// Global loads go through buffer resources: a descriptor per K/V block whose
+// range ends at the block's last valid key, so keys past the end read as 0
+// with no branch and no address arithmetic per block.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
 template <int D, bool CAUSAL, bool VARLEN, typename OutT>
 __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     using T = Tile<D>;
-    __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::K_ELEMS + 2 * T::V_ELEMS];
+    unsigned short *const Kbuf0 = smem;
+    unsigned short *const Kbuf1 = smem + T::K_ELEMS;
+    unsigned short *const Vbuf0 = smem + 2 * T::K_ELEMS;
+    unsigned short *const Vbuf1 = smem + 2 * T::K_ELEMS + T::V_ELEMS;
 
     TileCoord tc;
     const bool ok = VARLEN ? decode_varlen(blockIdx.x, p, tc) : decode_fixed(blockIdx.x, p, tc);
@@ -236,7 +253,9 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     const int qrow = qw0 + lq;            // query row of this lane
     const bool row_ok = qrow < Nq;
     const int64_t tok = (int64_t)p.H * D; // elements between consecutive tokens
+    const unsigned tokb = (unsigned)(tok * 2);   // ... in bytes
     const int causal_shift = Nk - Nq;     // bottom-right alignment
+    const int wave_last_row = min(qw0 + 31, Nq - 1);
 
     const unsigned short *Qg = (const unsigned short *)p.q + (int64_t)tc.q_tok0 * tok + tc.h * D;
     const unsigned short *Kg = (const unsigned short *)p.k + (int64_t)tc.k_tok0 * tok + tc.h * D;
@@ -249,15 +268,29 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         const int kmax = last_row + causal_shift;
         nblocks = kmax < 0 ? 0 : min(nblocks, kmax / T::BN + 1);
     }
+    // Bytes of the block's valid rows: the range of its buffer descriptor.
+    auto block_bytes = [&](int kb) -> unsigned {
+        const int rem = Nk - kb * T::BN;
+        if (kb >= nblocks || rem <= 0) return 0u;
+        return (unsigned)(min(rem, T::BN) - 1) * tokb + (unsigned)(D * 2);
+    };
+    auto active = [&](int kb) -> bool {   // does this wave have a live key in block kb?
+        return qw0 < Nq && (!CAUSAL || kb * T::BN <= wave_last_row + causal_shift);
+    };
 
     // Q fragments: B operand of S^T = K Q^T (query = lane % 32, 8 dims per half).
     bf16x8 qf[T::NDS];
+    {
+        const int rows = min(T::BM, Nq - m0);
+        const __amdgpu_buffer_rsrc_t rq =
+            make_rsrc(Qg + (int64_t)m0 * tok, (unsigned)(rows - 1) * tokb + (unsigned)(D * 2));
+        const unsigned qoff = (unsigned)(32 * w + lq) * tokb + (unsigned)(16 * g);
 #pragma unroll
-    for (int ds = 0; ds < T::NDS; ++ds) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row_ok) x = *(const u32x4 *)(Qg + (int64_t)qrow * tok + 16 * ds + 8 * g);
-        x = (x ^ p.q_xor) & p.q_and;        // sign flip (scale < 0) or zero (scale = 0)
-        qf[ds] = __builtin_bit_cast(bf16x8, x);
+        for (int ds = 0; ds < T::NDS; ++ds) {
+            u32x4 x = buffer_load16(rq, qoff + 32u * ds);
+            x = (x ^ p.q_xor) & p.q_and;      // sign flip (scale < 0) or zero (scale = 0)
+            qf[ds] = __builtin_bit_cast(bf16x8, x);
+        }
     }
 
     f32x16 oacc[T::NDT];
@@ -272,191 +305,255 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     const float c = p.scale_log2;
     const float tau = p.threshold;
 
+    // Per-thread load/store coordinates, fixed for the whole tile.
+    unsigned k_voff[T::KPT];
+    int k_lds[T::KPT];
+#pragma unroll
+    for (int rr = 0; rr < T::KPT; ++rr) {
+        const int u = tid + rr * T::NT;
+        const int row = u / (D / 8), cc = u % (D / 8);
+        k_voff[rr] = (unsigned)row * tokb + 16u * cc;
+        k_lds[rr] = row * T::KS + 8 * cc;
+    }
+    unsigned v_voff[T::VPT];
+    int v_lds[T::VPT];
+    bool v_mine[T::VPT];
+#pragma unroll
+    for (int rr = 0; rr < T::VPT; ++rr) {
+        const int u = tid + rr * T::NT;
+        v_mine[rr] = u < T::VU;
+        const int kp = (u % (T::BN / 2)), cc = (u / (T::BN / 2)) % (D / 8);
+        const int key = 2 * kp;
+        v_voff[rr] = (unsigned)key * tokb + 16u * cc;
+        v_lds[rr] = 8 * cc * T::VS + (key & ~15) + vt_pos16(key & 15);
+    }
+
     u32x4 kreg[T::KPT];
     u32x4 vreg[T::VPT][2];
 
-    auto load_block = [&](int kb) {
-        const int kv0 = kb * T::BN;
+    auto load_k = [&](int kb) {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)kb * T::BN * tok, block_bytes(kb));
 #pragma unroll
-        for (int rr = 0; rr < T::KPT; ++rr) {
-            const int u = tid + rr * T::NT;
-            const int row = u / (D / 8), cc = u % (D / 8);
-            const int key = kv0 + row;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (key < Nk) x = *(const u32x4 *)(Kg + (int64_t)key * tok + 8 * cc);
-            kreg[rr] = x;
-        }
+        for (int rr = 0; rr < T::KPT; ++rr) kreg[rr] = buffer_load16(rk, k_voff[rr]);
+    };
+    auto load_v = [&](int kb) {
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)kb * T::BN * tok, block_bytes(kb));
 #pragma unroll
         for (int rr = 0; rr < T::VPT; ++rr) {
-            const int u = tid + rr * T::NT;
-            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-            if (u < T::VU) {
-                const int kp = u % (T::BN / 2), cc = u / (T::BN / 2);
-                const int key = kv0 + 2 * kp;
-                if (key < Nk) x0 = *(const u32x4 *)(Vg + (int64_t)key * tok + 8 * cc);
-                if (key + 1 < Nk) x1 = *(const u32x4 *)(Vg + (int64_t)(key + 1) * tok + 8 * cc);
-            }
-            vreg[rr][0] = x0;
-            vreg[rr][1] = x1;
+            vreg[rr][0] = buffer_load16(rv, v_voff[rr]);
+            vreg[rr][1] = buffer_load16(rv, v_voff[rr] + tokb);
         }
     };
-
-    auto store_block = [&](int buf) {
-        unsigned short *Ks = smem + buf * T::STAGE;
-        unsigned short *Vt = Ks + T::K_ELEMS;
+    auto store_k = [&](unsigned short *Ks) {
 #pragma unroll
-        for (int rr = 0; rr < T::KPT; ++rr) {
-            const int u = tid + rr * T::NT;
-            const int row = u / (D / 8), cc = u % (D / 8);
-            *(u32x4 *)(Ks + row * T::KS + 8 * cc) = kreg[rr];
-        }
+        for (int rr = 0; rr < T::KPT; ++rr) *(u32x4 *)(Ks + k_lds[rr]) = kreg[rr];
+    };
+    auto store_v = [&](unsigned short *Vt) {
 #pragma unroll
         for (int rr = 0; rr < T::VPT; ++rr) {
-            const int u = tid + rr * T::NT;
-            if (u < T::VU) {
-                const int kp = u % (T::BN / 2), cc = u / (T::BN / 2);
-                const int key = 2 * kp;
-                const int col = (key & ~15) + vt_pos16(key & 15);   // even; key+1 lands at col+1
+            if (v_mine[rr]) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const unsigned a = vreg[rr][0][e >> 1], b = vreg[rr][1][e >> 1];
                     const unsigned word = (e & 1) ? ((a >> 16) | (b & 0xffff0000u))
                                                   : ((a & 0xffffu) | (b << 16));
-                    *(unsigned *)(Vt + (8 * cc + e) * T::VS + col) = word;
+                    *(unsigned *)(Vt + v_lds[rr] + e * T::VS) = word;
                 }
             }
         }
     };
 
-    if (nblocks > 0) {
-        load_block(0);
-        store_block(0);
-        __syncthreads();
-    }
-
-    for (int kb = 0; kb < nblocks; ++kb) {
-        const int buf = kb & 1;
-        const bool more = kb + 1 < nblocks;
-        if (more) load_block(kb + 1);
-
-        const int kv0 = kb * T::BN;
-        const int wave_last_row = min(qw0 + 31, Nq - 1);
-        const bool active = qw0 < Nq && (!CAUSAL || kv0 <= wave_last_row + causal_shift);
-        if (active) {
-            const unsigned short *Ks = smem + buf * T::STAGE;
-            const unsigned short *Vt = Ks + T::K_ELEMS;
-
-            // S^T = K Q^T for the BN keys of the block.
-            f32x16 s[T::NKT];
+    // S^T = K Q^T for the BN keys of a block.
+    auto qk = [&](const unsigned short *Ks, f32x16 (&s)[T::NKT]) {
 #pragma unroll
-            for (int kt = 0; kt < T::NKT; ++kt)
+        for (int kt = 0; kt < T::NKT; ++kt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+            for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
-            for (int ds = 0; ds < T::NDS; ++ds) {
+        for (int ds = 0; ds < T::NDS; ++ds) {
 #pragma unroll
-                for (int kt = 0; kt < T::NKT; ++kt) {
-                    const bf16x8 kf = *(const bf16x8 *)(Ks + (32 * kt + lq) * T::KS + 16 * ds + 8 * g);
-                    s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt], 0, 0, 0);
-                }
-            }
-
-            // Mask keys past the end and, for causal, after the row's last key.
-            const bool need_mask = (kv0 + T::BN > Nk) ||
-                                   (CAUSAL && kv0 + T::BN - 1 > qw0 + causal_shift);
-            if (need_mask) {
-                const int lim = CAUSAL ? min(Nk - 1, qrow + causal_shift) : Nk - 1;
-#pragma unroll
-                for (int kt = 0; kt < T::NKT; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kv0 + 32 * kt + 8 * (i >> 2) + 4 * g + (i & 3);
-                        if (key > lim) s[kt][i] = -INFINITY;
-                    }
-            }
-
-            // Row maximum of the block and the rescale decision.
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < T::NKT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-            mx = lane_pair_max(mx);
-            const float cand = fmaxf(r, mx);
-            float alpha = 1.f;
-            if (cand != -INFINITY) {
-                if (r == -INFINITY) {
-                    // First block with a live key: take the candidate; the
-                    // state is still zero, so alpha = 0 (exp2 of delta = -inf).
-                    r = cand;
-                    alpha = 0.f;
-                } else {
-                    const float delta = (r - cand) * c;
-                    if (!(delta >= -tau)) {
-                        r = cand;
-                        alpha = __builtin_amdgcn_exp2f(delta);
-                    }
-                }
-            }
-            const float neg_rc = (r == -INFINITY) ? 0.f : -r * c;
-
-            // P = exp2(S*c - r*c), rounded to bf16 for the PV MFMA.  The row
-            // sum is taken over the same bf16 values (v_dot2 with (1, 1)), so
-            // numerator and denominator see identical weights.
-            float fsum0 = 0.f, fsum1 = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < T::NKT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, neg_rc));
-                    s[kt][i] = pv;
-                    if (i & 1) fsum1 += pv; else fsum0 += pv;
-                }
-
-            // (Words are kept in scalars: a bit cast of a vector element
-            // reads element 0 in this compiler.)
-            float bsum0 = 0.f, bsum1 = 0.f;
-            bf16x8 pf[T::NKS];
-#pragma unroll
-            for (int ks = 0; ks < T::NKS; ++ks) {
-                const f32x16 &src = s[ks >> 1];
-                const int i0 = 8 * (ks & 1);
-                const unsigned w0 = pack_bf16x2(src[i0 + 0], src[i0 + 1]);
-                const unsigned w1 = pack_bf16x2(src[i0 + 2], src[i0 + 3]);
-                const unsigned w2 = pack_bf16x2(src[i0 + 4], src[i0 + 5]);
-                const unsigned w3 = pack_bf16x2(src[i0 + 6], src[i0 + 7]);
-                bsum0 = add_bf16x2(w0, bsum0);
-                bsum1 = add_bf16x2(w1, bsum1);
-                bsum0 = add_bf16x2(w2, bsum0);
-                bsum1 = add_bf16x2(w3, bsum1);
-                const u32x4 x = {w0, w1, w2, w3};
-                pf[ks] = __builtin_bit_cast(bf16x8, x);
-            }
-            lsum = lsum * alpha + (bsum0 + bsum1);
-            lsum32 = lsum32 * alpha + (fsum0 + fsum1);
-
-            // Conditional rescale of the accumulator, skipped per wave when no
-            // row of the wave moved its reference.
-            if (__ballot(alpha != 1.f)) {
-#pragma unroll
-                for (int dt = 0; dt < T::NDT; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-            }
-
-            // O^T += V^T P^T.
-#pragma unroll
-            for (int ks = 0; ks < T::NKS; ++ks) {
-#pragma unroll
-                for (int dt = 0; dt < T::NDT; ++dt) {
-                    const bf16x8 vf = *(const bf16x8 *)(Vt + (32 * dt + lq) * T::VS + 16 * ks + 8 * g);
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[dt], 0, 0, 0);
-                }
+            for (int kt = 0; kt < T::NKT; ++kt) {
+                const bf16x8 kf = *(const bf16x8 *)(Ks + (32 * kt + lq) * T::KS + 16 * ds + 8 * g);
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt], 0, 0, 0);
             }
         }
+    };
 
-        if (more) store_block(buf ^ 1);
+    // O^T += V^T P^T, after the conditional rescale of O by alpha.
+    auto rescale = [&](float alpha) {
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        }
+    };
+    auto pv = [&](const unsigned short *Vt, const bf16x8 (&pf)[T::NKS]) {
+#pragma unroll
+        for (int ks = 0; ks < T::NKS; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < T::NDT; ++dt) {
+                const bf16x8 vf = *(const bf16x8 *)(Vt + (32 * dt + lq) * T::VS + 16 * ks + 8 * g);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[dt], 0, 0, 0);
+            }
+        }
+    };
+
+    // Mask keys past the end and, for causal, after the row's last key (set
+    // to -inf before the maximum).  Only blocks that cross a boundary pay.
+    auto mask_block = [&](int kb, f32x16 (&s)[T::NKT]) {
+        const int kv0 = kb * T::BN;
+        const bool need_mask = (kv0 + T::BN > Nk) ||
+                               (CAUSAL && kv0 + T::BN - 1 > qw0 + causal_shift);
+        if (need_mask) {
+            // Lane's last usable key, relative to its first key in the block.
+            const int lim = (CAUSAL ? min(Nk - 1, qrow + causal_shift) : Nk - 1) - kv0 - 4 * g;
+#pragma unroll
+            for (int kt = 0; kt < T::NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) s[kt][i] = -INFINITY;
+        }
+    };
+
+    // Online softmax of one (masked) block: row max, rescale decision,
+    // P = exp2, row sums, bf16 P.  Branch-free, so it can interleave with the
+    // MFMAs of the previous block's PV product.  Returns alpha for O.
+    auto softmax = [&](f32x16 (&s)[T::NKT], bf16x8 (&pf)[T::NKS]) -> float {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < T::NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+        mx = lane_pair_max(mx);
+        const float cand = fmaxf(r, mx);
+        // No live key so far (cand = -inf): keep r = -inf, alpha = 1.
+        // First live block (r = -inf): take cand, alpha = exp2(-inf) = 0.
+        // Otherwise keep r while delta = (r - cand) * c >= -tau.
+        const bool live = cand != -INFINITY;
+        const bool first = r == -INFINITY;
+        const float delta = first ? -INFINITY : (r - cand) * c;
+        const bool move = live && !(delta >= -tau);
+        const float alpha = move ? __builtin_amdgcn_exp2f(delta) : 1.f;
+        r = move ? cand : r;
+        const float neg_rc = (r == -INFINITY) ? 0.f : -r * c;
+
+        // P = exp2(S*c - r*c), rounded to bf16 for the PV MFMA.  The row sum
+        // for O is taken over the same bf16 values (v_dot2 with (1, 1)), so
+        // numerator and denominator see identical weights; the fp32 sum
+        // feeds LSE.  (Words are kept in scalars: a bit cast of a vector
+        // element reads element 0 in this compiler.)
+        float fsum0 = 0.f, fsum1 = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < T::NKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv_ = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, neg_rc));
+                s[kt][i] = pv_;
+                if (i & 1) fsum1 += pv_; else fsum0 += pv_;
+            }
+        float bsum0 = 0.f, bsum1 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < T::NKS; ++ks) {
+            const f32x16 &src = s[ks >> 1];
+            const int i0 = 8 * (ks & 1);
+            const unsigned w0 = pack_bf16x2(src[i0 + 0], src[i0 + 1]);
+            const unsigned w1 = pack_bf16x2(src[i0 + 2], src[i0 + 3]);
+            const unsigned w2 = pack_bf16x2(src[i0 + 4], src[i0 + 5]);
+            const unsigned w3 = pack_bf16x2(src[i0 + 6], src[i0 + 7]);
+            bsum0 = add_bf16x2(w0, bsum0);
+            bsum1 = add_bf16x2(w1, bsum1);
+            bsum0 = add_bf16x2(w2, bsum0);
+            bsum1 = add_bf16x2(w3, bsum1);
+            const u32x4 x = {w0, w1, w2, w3};
+            pf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+        lsum = lsum * alpha + (bsum0 + bsum1);
+        lsum32 = lsum32 * alpha + (fsum0 + fsum1);
+        return alpha;
+    };
+
+    // One pipelined step: S_kb = Q K_kb^T, then O += P_{kb-1} V_{kb-1} while
+    // the softmax of block kb runs.  K_kb is in Kc, V_{kb-1} in Vp; the
+    // prefetched K_{kb+1} and V_kb are written to Kn and Vn.  P_j lives in
+    // pfA for even j and pfB for odd j.  The mask code is compiled only into
+    // the steps of blocks that cross a boundary (mask_tag true).
+    f32x16 s[T::NKT];
+    bf16x8 pfA[T::NKS], pfB[T::NKS];
+    float alphaA = 1.f, alphaB = 1.f;
+    auto step = [&](auto mask_tag, int kb, const unsigned short *Kc, const unsigned short *Vp,
+                    unsigned short *Kn, unsigned short *Vn,
+                    const bf16x8 (&p_in)[T::NKS], float alpha_in,
+                    bf16x8 (&p_out)[T::NKS], float &alpha_out) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        load_k(kb + 1);
+        load_v(kb);
+        // A wave's live blocks are a prefix 0..last of the tile's blocks, so
+        // for kb >= 1 "live kb" implies "live kb-1".
+        if (active(kb)) {
+            qk(Kc, s);
+            if constexpr (MASK) mask_block(kb, s);
+            rescale(alpha_in);
+            pv(Vp, p_in);
+            alpha_out = softmax(s, p_out);
+            // One basic block holds the PV MFMAs and the softmax VALU work:
+            // interleave them so the wave issues VALU while its MFMAs run.
+#pragma unroll
+            for (int i = 0; i < T::NKS * T::NDT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
+            }
+        } else if (active(kb - 1)) {
+            rescale(alpha_in);
+            pv(Vp, p_in);
+        }
+        store_k(Kn);
+        store_v(Vn);
         __syncthreads();
+    };
+    using NoMask = std::integral_constant<bool, false>;
+    using Mask = std::integral_constant<bool, true>;
+
+    // Blocks below n_full need no mask for any row of the tile.
+    int n_full = Nk / T::BN;
+    if (CAUSAL) n_full = min(n_full, max(0, (m0 + causal_shift + 1) / T::BN));
+
+    if (nblocks > 0) {
+        load_k(0);
+        store_k(Kbuf0);
+        __syncthreads();
+        load_k(1);
+        load_v(0);
+        if (active(0)) {
+            qk(Kbuf0, s);
+            mask_block(0, s);
+            alphaA = softmax(s, pfA);
+        }
+        store_k(Kbuf1);
+        store_v(Vbuf0);
+        __syncthreads();
+    }
+    int kb = 1;
+    for (; kb + 1 < n_full; kb += 2) {
+        step(NoMask{}, kb, Kbuf1, Vbuf0, Kbuf0, Vbuf1, pfA, alphaA, pfB, alphaB);
+        step(NoMask{}, kb + 1, Kbuf0, Vbuf1, Kbuf1, Vbuf0, pfB, alphaB, pfA, alphaA);
+    }
+    // kb is odd here, so the same buffer parity as above applies.
+    for (; kb < nblocks; kb += 2) {
+        step(Mask{}, kb, Kbuf1, Vbuf0, Kbuf0, Vbuf1, pfA, alphaA, pfB, alphaB);
+        if (kb + 1 < nblocks)
+            step(Mask{}, kb + 1, Kbuf0, Vbuf1, Kbuf1, Vbuf0, pfB, alphaB, pfA, alphaA);
+    }
+    if (nblocks > 0 && active(nblocks - 1)) {
+        // P of the last block is in pfB when its index is odd, pfA when even.
+        if ((nblocks - 1) & 1) {
+            rescale(alphaB);
+            pv(Vbuf1, pfB);
+        } else {
+            rescale(alphaA);
+            pv(Vbuf0, pfA);
+        }
     }
 
     // Epilogue: O = o / l, LSE = ln l + r * scale.
