@@ -67,6 +67,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D_>
 struct Tile {
@@ -76,9 +79,9 @@ struct Tile {
     static constexpr int BM = kBlockM;
     static constexpr int NT = 64 * NW;        // threads per workgroup
     static constexpr int KS = D + 8;          // K row stride in LDS (bf16 elements)
-    static constexpr int VS = BN + 8;         // V^T row stride in LDS
+    static constexpr int VS = D + 16;         // V row stride in LDS (transpose reads)
     static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = D * VS;
+    static constexpr int V_ELEMS = BN * VS;
     static constexpr int LDS_BYTES = (2 * K_ELEMS + 2 * V_ELEMS) * 2;
     static constexpr int NKT = BN / 32;       // 32-key tiles of S^T per block
     static constexpr int NDS = D / 16;        // 16-wide head-dim steps of S^T
@@ -86,8 +89,6 @@ struct Tile {
     static constexpr int NKS = BN / 16;       // 16-key steps of O^T
     static constexpr int KCH = BN * D / 8;    // 16-byte chunks in a K block
     static constexpr int KPT = KCH / NT;      // ... per thread
-    static constexpr int VU = (BN / 2) * (D / 8);   // (key pair, 8-dim chunk) units of a V block
-    static constexpr int VPT = (VU + NT - 1) / NT;
     static_assert(KCH % NT == 0, "K block must split evenly over the threads");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -101,13 +102,6 @@ __device__ __forceinline__ float lane_pair_max(float x) {
 __device__ __forceinline__ float lane_pair_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Position of key kappa (0..15) inside its 16-key group of V^T in LDS: the
-// S^T accumulator hands slot j of half g the key 8*(j/4) + 4*g + j%4, and the
-// V^T operand of the same MFMA reads positions 8*g + j.
-__device__ __forceinline__ int vt_pos16(int kappa) {
-    return ((kappa >> 2) & 1) * 8 + (kappa & 3) + ((kappa >> 3) << 2);
 }
 
 // Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
@@ -243,7 +237,9 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     if (!ok) return;   // uniform over the workgroup
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    // Wave index, known wave-uniform (SGPR): keeps per-wave decisions and
+    // the buffer descriptors that depend on it scalar.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int lq = lane & 31;
     const int g = lane >> 5;
@@ -305,66 +301,73 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     const float c = p.scale_log2;
     const float tau = p.threshold;
 
-    // Per-thread load/store coordinates, fixed for the whole tile.
-    unsigned k_voff[T::KPT];
-    int k_lds[T::KPT];
+    // ---------------------------------------------------------------------
+    // Ping-pong schedule.  The 8 waves form two groups: waves 0-3 and 4-7;
+    // wave w and wave w+4 share a SIMD.  Each iteration j of a wave has an
+    // MFMA phase M(j) -- rescale O, S_j = Q K_j^T, O += P_{j-1} V_{j-1} --
+    // and a VALU phase V(j) -- softmax of block j, LDS writes of prefetched
+    // K/V, next global loads.  Group 1 runs one phase behind group 0, so on
+    // every SIMD one wave issues MFMAs while the other issues VALU work.
+    // Phases are separated by workgroup barriers; every wave executes the
+    // same number of barriers.
+    //
+    //   slot 2j  : group 0 M(j)   group 1 V(j-1)
+    //   slot 2j+1: group 0 V(j)   group 1 M(j)
+    //
+    // K_b lives in Kbuf[b % 2], V_b in Vbuf[b % 2].  Group g loads its part
+    // of each block (K rows 32g..32g+31; V^T head-dim half g); in V(j) it
+    // writes K_{j+1+g} and V_{j+g} (staged in registers one V phase earlier)
+    // and issues the loads of K_{j+2+g} and V_{j+1+g}.  Every buffer is
+    // written only after both groups' last reads of its previous block and
+    // before the first read of the new one (one barrier apart).
+    // ---------------------------------------------------------------------
+    const int grp = w >> 2;
+    const int gtid = tid & 255;
+
+    // Per-thread load/store coordinates for this group's part of a block.
+    constexpr int KPT2 = (32 * D / 8) / 256;        // 16-byte K chunks per thread
+    static_assert(KPT2 >= 1 && (32 * D / 8) % 256 == 0, "K half must split over 256 threads");
+    unsigned k_voff[KPT2];
+    int k_lds[KPT2];
 #pragma unroll
-    for (int rr = 0; rr < T::KPT; ++rr) {
-        const int u = tid + rr * T::NT;
-        const int row = u / (D / 8), cc = u % (D / 8);
+    for (int rr = 0; rr < KPT2; ++rr) {
+        const int u = gtid + rr * 256;
+        const int row = 32 * grp + u / (D / 8), cc = u % (D / 8);
         k_voff[rr] = (unsigned)row * tokb + 16u * cc;
         k_lds[rr] = row * T::KS + 8 * cc;
     }
-    unsigned v_voff[T::VPT];
-    int v_lds[T::VPT];
-    bool v_mine[T::VPT];
+    int v_lds[KPT2];
 #pragma unroll
-    for (int rr = 0; rr < T::VPT; ++rr) {
-        const int u = tid + rr * T::NT;
-        v_mine[rr] = u < T::VU;
-        const int kp = (u % (T::BN / 2)), cc = (u / (T::BN / 2)) % (D / 8);
-        const int key = 2 * kp;
-        v_voff[rr] = (unsigned)key * tokb + 16u * cc;
-        v_lds[rr] = 8 * cc * T::VS + (key & ~15) + vt_pos16(key & 15);
+    for (int rr = 0; rr < KPT2; ++rr) {
+        const int u = gtid + rr * 256;
+        v_lds[rr] = (32 * grp + u / (D / 8)) * T::VS + 8 * (u % (D / 8));
     }
 
-    u32x4 kreg[T::KPT];
-    u32x4 vreg[T::VPT][2];
+    u32x4 kreg[KPT2];
+    u32x4 vreg[KPT2];
 
     auto load_k = [&](int kb) {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)kb * T::BN * tok, block_bytes(kb));
 #pragma unroll
-        for (int rr = 0; rr < T::KPT; ++rr) kreg[rr] = buffer_load16(rk, k_voff[rr]);
+        for (int rr = 0; rr < KPT2; ++rr) kreg[rr] = buffer_load16(rk, k_voff[rr]);
     };
     auto load_v = [&](int kb) {
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)kb * T::BN * tok, block_bytes(kb));
 #pragma unroll
-        for (int rr = 0; rr < T::VPT; ++rr) {
-            vreg[rr][0] = buffer_load16(rv, v_voff[rr]);
-            vreg[rr][1] = buffer_load16(rv, v_voff[rr] + tokb);
-        }
+        for (int rr = 0; rr < KPT2; ++rr) vreg[rr] = buffer_load16(rv, k_voff[rr]);
     };
     auto store_k = [&](unsigned short *Ks) {
 #pragma unroll
-        for (int rr = 0; rr < T::KPT; ++rr) *(u32x4 *)(Ks + k_lds[rr]) = kreg[rr];
+        for (int rr = 0; rr < KPT2; ++rr) *(u32x4 *)(Ks + k_lds[rr]) = kreg[rr];
     };
-    auto store_v = [&](unsigned short *Vt) {
+    auto store_v = [&](unsigned short *Vs) {
 #pragma unroll
-        for (int rr = 0; rr < T::VPT; ++rr) {
-            if (v_mine[rr]) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const unsigned a = vreg[rr][0][e >> 1], b = vreg[rr][1][e >> 1];
-                    const unsigned word = (e & 1) ? ((a >> 16) | (b & 0xffff0000u))
-                                                  : ((a & 0xffffu) | (b << 16));
-                    *(unsigned *)(Vt + v_lds[rr] + e * T::VS) = word;
-                }
-            }
-        }
+        for (int rr = 0; rr < KPT2; ++rr) *(u32x4 *)(Vs + v_lds[rr]) = vreg[rr];
     };
 
     // S^T = K Q^T for the BN keys of a block.
-    auto qk = [&](const unsigned short *Ks, f32x16 (&s)[T::NKT]) {
+    f32x16 s[T::NKT];
+    auto qk = [&](const unsigned short *Ks) {
 #pragma unroll
         for (int kt = 0; kt < T::NKT; ++kt)
 #pragma unroll
@@ -380,7 +383,9 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     };
 
     // O^T += V^T P^T, after the conditional rescale of O by alpha.
-    auto rescale = [&](float alpha) {
+    bf16x8 pf[T::NKS];
+    float alpha = 1.f;
+    auto rescale = [&]() {
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt)
@@ -388,12 +393,22 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
                 for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
         }
     };
-    auto pv = [&](const unsigned short *Vt, const bf16x8 (&pf)[T::NKS]) {
+    // V^T operand by transpose reads of the row-major V tile: source lane s
+    // of each 16-lane group addresses V[row + s/4][col + 4*(s%4) .. +3], and
+    // ds_read_b64_tr_b16 returns to lane i, element e, V[row + e][col + i].
+    // Two reads give slots 0-3 (keys 4g..4g+3) and 4-7 (keys 8+4g..8+4g+3)
+    // of the 16-key step, the key order of the P^T operand.
+    const int tr_off = (4 * g + ((lane & 15) >> 2)) * T::VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto pv = [&](const unsigned short *Vs) {
 #pragma unroll
         for (int ks = 0; ks < T::NKS; ++ks) {
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt) {
-                const bf16x8 vf = *(const bf16x8 *)(Vt + (32 * dt + lq) * T::VS + 16 * ks + 8 * g);
+                const unsigned short *a0 = Vs + tr_off + 16 * ks * T::VS + 32 * dt;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a0);
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + 8 * T::VS));
+                const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[dt], 0, 0, 0);
             }
         }
@@ -401,7 +416,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
 
     // Mask keys past the end and, for causal, after the row's last key (set
     // to -inf before the maximum).  Only blocks that cross a boundary pay.
-    auto mask_block = [&](int kb, f32x16 (&s)[T::NKT]) {
+    auto mask_block = [&](int kb) {
         const int kv0 = kb * T::BN;
         const bool need_mask = (kv0 + T::BN > Nk) ||
                                (CAUSAL && kv0 + T::BN - 1 > qw0 + causal_shift);
@@ -416,10 +431,9 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         }
     };
 
-    // Online softmax of one (masked) block: row max, rescale decision,
-    // P = exp2, row sums, bf16 P.  Branch-free, so it can interleave with the
-    // MFMAs of the previous block's PV product.  Returns alpha for O.
-    auto softmax = [&](f32x16 (&s)[T::NKT], bf16x8 (&pf)[T::NKS]) -> float {
+    // Online softmax of one masked block: row max, rescale decision,
+    // P = exp2, row sums, bf16 P; sets alpha for the accumulator.
+    auto softmax = [&]() {
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < T::NKT; ++kt)
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         const bool first = r == -INFINITY;
         const float delta = first ? -INFINITY : (r - cand) * c;
         const bool move = live && !(delta >= -tau);
-        const float alpha = move ? __builtin_amdgcn_exp2f(delta) : 1.f;
+        alpha = move ? __builtin_amdgcn_exp2f(delta) : 1.f;
         r = move ? cand : r;
         const float neg_rc = (r == -INFINITY) ? 0.f : -r * c;
 
@@ -470,90 +484,60 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         }
         lsum = lsum * alpha + (bsum0 + bsum1);
         lsum32 = lsum32 * alpha + (fsum0 + fsum1);
-        return alpha;
     };
 
-    // One pipelined step: S_kb = Q K_kb^T, then O += P_{kb-1} V_{kb-1} while
-    // the softmax of block kb runs.  K_kb is in Kc, V_{kb-1} in Vp; the
-    // prefetched K_{kb+1} and V_kb are written to Kn and Vn.  P_j lives in
-    // pfA for even j and pfB for odd j.  The mask code is compiled only into
-    // the steps of blocks that cross a boundary (mask_tag true).
-    f32x16 s[T::NKT];
-    bf16x8 pfA[T::NKS], pfB[T::NKS];
-    float alphaA = 1.f, alphaB = 1.f;
-    auto step = [&](auto mask_tag, int kb, const unsigned short *Kc, const unsigned short *Vp,
-                    unsigned short *Kn, unsigned short *Vn,
-                    const bf16x8 (&p_in)[T::NKS], float alpha_in,
-                    bf16x8 (&p_out)[T::NKS], float &alpha_out) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        load_k(kb + 1);
-        load_v(kb);
-        // A wave's live blocks are a prefix 0..last of the tile's blocks, so
-        // for kb >= 1 "live kb" implies "live kb-1".
-        if (active(kb)) {
-            qk(Kc, s);
-            if constexpr (MASK) mask_block(kb, s);
-            rescale(alpha_in);
-            pv(Vp, p_in);
-            alpha_out = softmax(s, p_out);
-            // One basic block holds the PV MFMAs and the softmax VALU work:
-            // interleave them so the wave issues VALU while its MFMAs run.
-#pragma unroll
-            for (int i = 0; i < T::NKS * T::NDT; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // VALU
-            }
-        } else if (active(kb - 1)) {
-            rescale(alpha_in);
-            pv(Vp, p_in);
+    // The two phases.  j ranges: M(0..n), V(-1..n-1); out-of-range parts
+    // are skipped (uniform per wave).
+    const int n = nblocks;
+    auto m_phase = [&](int j, const unsigned short *Kc, const unsigned short *Vp) {
+        const bool do_pv = j >= 1 && j <= n && active(j - 1);
+        const bool do_qk = j < n && active(j);
+        if (do_pv) rescale();
+        if (do_qk) qk(Kc);
+        if (do_pv) pv(Vp);
+    };
+    auto v_phase = [&](int j, unsigned short *Kw, unsigned short *Vw) {
+        if (j + 1 + grp < n) store_k(Kw);
+        if (j + grp < n) store_v(Vw);
+        load_k(j + 2 + grp);     // range 0 (reads nothing) past the last block
+        load_v(j + 1 + grp);
+        if (j >= 0 && j < n && active(j)) {
+            mask_block(j);
+            softmax();
         }
-        store_k(Kn);
-        store_v(Vn);
-        __syncthreads();
     };
-    using NoMask = std::integral_constant<bool, false>;
-    using Mask = std::integral_constant<bool, true>;
 
-    // Blocks below n_full need no mask for any row of the tile.
-    int n_full = Nk / T::BN;
-    if (CAUSAL) n_full = min(n_full, max(0, (m0 + causal_shift + 1) / T::BN));
-
-    if (nblocks > 0) {
+    if (n > 0) {
         load_k(0);
         store_k(Kbuf0);
-        __syncthreads();
         load_k(1);
         load_v(0);
-        if (active(0)) {
-            qk(Kbuf0, s);
-            mask_block(0, s);
-            alphaA = softmax(s, pfA);
-        }
-        store_k(Kbuf1);
-        store_v(Vbuf0);
         __syncthreads();
-    }
-    int kb = 1;
-    for (; kb + 1 < n_full; kb += 2) {
-        step(NoMask{}, kb, Kbuf1, Vbuf0, Kbuf0, Vbuf1, pfA, alphaA, pfB, alphaB);
-        step(NoMask{}, kb + 1, Kbuf0, Vbuf1, Kbuf1, Vbuf0, pfB, alphaB, pfA, alphaA);
-    }
-    // kb is odd here, so the same buffer parity as above applies.
-    for (; kb < nblocks; kb += 2) {
-        step(Mask{}, kb, Kbuf1, Vbuf0, Kbuf0, Vbuf1, pfA, alphaA, pfB, alphaB);
-        if (kb + 1 < nblocks)
-            step(Mask{}, kb + 1, Kbuf0, Vbuf1, Kbuf1, Vbuf0, pfB, alphaB, pfA, alphaA);
-    }
-    if (nblocks > 0 && active(nblocks - 1)) {
-        // P of the last block is in pfB when its index is odd, pfA when even.
-        if ((nblocks - 1) & 1) {
-            rescale(alphaB);
-            pv(Vbuf1, pfB);
-        } else {
-            rescale(alphaA);
-            pv(Vbuf0, pfA);
+        // Group 1 starts with V(-1) (LDS writes of K_1 and V_0, loads of the
+        // next blocks) while group 0 runs M(0); from then on both groups run
+        // M(j), V(j) pairs, group 1 one phase behind.  Group 0 ends with one
+        // extra barrier so both groups meet the same number of barriers.
+        // V(j) writes K_{j+1+grp} to Kbuf[(j+1+grp)%2] and V_{j+grp} to
+        // Vbuf[(j+grp)%2].
+        unsigned short *const Kw_even = grp ? Kbuf0 : Kbuf1;   // j even
+        unsigned short *const Vw_even = grp ? Vbuf1 : Vbuf0;
+        unsigned short *const Kw_odd = grp ? Kbuf1 : Kbuf0;    // j odd
+        unsigned short *const Vw_odd = grp ? Vbuf0 : Vbuf1;
+        if (grp == 1) {
+            v_phase(-1, Kw_odd, Vw_odd);
+            __syncthreads();
         }
+        for (int j = 0; j <= n; j += 2) {
+            m_phase(j, Kbuf0, Vbuf1);
+            __syncthreads();
+            v_phase(j, Kw_even, Vw_even);
+            __syncthreads();
+            m_phase(j + 1, Kbuf1, Vbuf0);
+            __syncthreads();
+            v_phase(j + 1, Kw_odd, Vw_odd);
+            __syncthreads();
+        }
+        if (grp == 0) __syncthreads();
     }
 
     // Epilogue: O = o / l, LSE = ln l + r * scale.
@@ -615,3 +599,4 @@ int launch_fwd(const FwdParams &p, int d, bool causal, OutType out, void *stream
 }
 
 }  // namespace fa
+
