@@ -52,7 +52,7 @@ def traffic_from_profile(workload: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    fields = dict(re.findall(r"^([a-z_]+):\s*(\S+)\s*$", text, flags=re.M))
+    fields = dict(re.findall(r"^([a-z0-9_]+):\s*(\S+)\s*$", text, flags=re.M))
     if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     try:
@@ -100,8 +100,9 @@ def cpu_baseline(w, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first; the clocks take a few hundred launches to settle")
     ap.add_argument("--config", type=int, default=3, help="workload 1-5 (3 = the headline)")
     ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,

@@ -6,6 +6,7 @@ are disabled for device code.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 
@@ -35,6 +36,9 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # Resolve every symbol now: a kernel whose launch stub the host pass did
+    # not emit would otherwise only fail when the library is loaded.
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     return LIB
 

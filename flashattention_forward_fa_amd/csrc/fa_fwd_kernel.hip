@@ -368,18 +368,30 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     // S^T = K Q^T for the BN keys of a block.
     f32x16 s[T::NKT];
     auto qk = [&](const unsigned short *Ks) {
+        constexpr int NR = T::NDS * T::NKT;
+        constexpr int AHEAD = NR < 8 ? NR : 8;
+        bf16x8 kf[T::NDS][T::NKT];
+#pragma unroll
+        for (int ds = 0; ds < T::NDS; ++ds)
+#pragma unroll
+            for (int kt = 0; kt < T::NKT; ++kt)
+                kf[ds][kt] = *(const bf16x8 *)(Ks + (32 * kt + lq) * T::KS + 16 * ds + 8 * g);
 #pragma unroll
         for (int kt = 0; kt < T::NKT; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
 #pragma unroll
-        for (int ds = 0; ds < T::NDS; ++ds) {
+        for (int ds = 0; ds < T::NDS; ++ds)
 #pragma unroll
-            for (int kt = 0; kt < T::NKT; ++kt) {
-                const bf16x8 kf = *(const bf16x8 *)(Ks + (32 * kt + lq) * T::KS + 16 * ds + 8 * g);
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt], 0, 0, 0);
-            }
+            for (int kt = 0; kt < T::NKT; ++kt)
+                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kt], qf[ds], s[kt], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+        for (int i = 0; i < NR - AHEAD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
     };
 
     // O^T += V^T P^T, after the conditional rescale of O by alpha.
