@@ -105,6 +105,8 @@ def main():
                     help="untimed steps first; the clocks take a few hundred launches to settle")
     ap.add_argument("--config", type=int, default=3, help="workload 1-5 (3 = the headline)")
     ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="grouped K/V heads for workloads 2-4 (0 = as many as query heads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -141,7 +143,7 @@ def main():
                           "GB_per_s": round(4 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return
     fa.load()
-    w = wl.config(args.config)
+    w = wl.grouped(args.config, args.kv_heads) if args.kv_heads else wl.config(args.config)
     q, k, v, off = parity.to_device(w)
     odt = fa.FA_DTYPE_F32 if w.o_dtype == "f32" else fa.FA_DTYPE_BF16
     o = torch.empty(q.shape, dtype=torch.float32 if odt else torch.bfloat16, device="cuda")
@@ -152,6 +154,7 @@ def main():
     opts = fa.fa_fwd_opts_default()
     opts.o_dtype = odt
     opts.rescale_threshold = args.tau
+    opts.kv_heads = w.kv_heads
     stream = torch.cuda.current_stream()
 
     def step():
@@ -176,6 +179,8 @@ def main():
     wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    sorted_ms = sorted(launch_ms)
+    median_launch_ms = sorted_ms[len(sorted_ms) // 2]
     ms_per_step = wall * 1e3 / args.steps
 
     flops = w.flops()
@@ -202,6 +207,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
                      "avg_launch_ms": round(avg_launch_ms, 5),
+                     "median_launch_ms": round(median_launch_ms, 5),
+                     "min_launch_ms": round(sorted_ms[0], 5),
                      "algorithmic_hbm_bytes": w.io_bytes()},
     }
     if args.cpu_seconds > 0:

@@ -40,7 +40,7 @@ class FaError(RuntimeError):
 class FaFwdOpts(ctypes.Structure):
     """Mirror of ``fa_fwd_opts`` in include/fa.h."""
     _fields_ = [("o_dtype", ctypes.c_int32), ("rescale_threshold", ctypes.c_float),
-                ("schedule", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -131,9 +131,11 @@ def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_s
               schedule: int = FA_SCHEDULE_AUTO, stream=None):
     """Allocate O and LSE with torch on q's device and run fa_fwd_ex.
 
-    Fixed length: q [B,Nq,H,d], k/v [B,Nk,H,d] bf16 -> o [B,Nq,H,d], lse [B,H,Nq].
-    Varlen: q/k/v [T,H,d] and int32 offsets [B+1] on the device, max_seqlen =
-    the longest sequence -> o [T,H,d], lse [H,T].
+    Fixed length: q [B,Nq,H,d], k/v [B,Nk,Hkv,d] bf16 -> o [B,Nq,H,d], lse [B,H,Nq].
+    Varlen: q [T,H,d], k/v [T,Hkv,d] and int32 offsets [B+1] on the device,
+    max_seqlen = the longest sequence -> o [T,H,d], lse [H,T].
+    Hkv (read from k's shape) divides H; query heads h*G .. h*G+G-1, G = H/Hkv,
+    share K/V head h.
     """
     import torch
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
@@ -144,14 +146,15 @@ def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_s
     o = torch.empty(q.shape, dtype=odt, device=q.device)
     if varlen_offsets is None:
         B, Nq, H, d = q.shape
-        Nk = k.shape[1]
-        if k.shape != (B, Nk, H, d) or v.shape != k.shape:
-            raise ValueError("k, v must be [B, Nk, H, d] matching q")
+        Nk, Hkv = k.shape[1], k.shape[2]
+        if k.shape != (B, Nk, Hkv, d) or v.shape != k.shape or Hkv < 1 or H % Hkv:
+            raise ValueError("k, v must be [B, Nk, Hkv, d] matching q, with Hkv dividing H")
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     else:
         T, H, d = q.shape
-        if k.shape != q.shape or v.shape != q.shape:
-            raise ValueError("packed q, k, v must have the same shape")
+        Hkv = k.shape[1]
+        if k.shape != (T, Hkv, d) or v.shape != k.shape or Hkv < 1 or H % Hkv:
+            raise ValueError("packed k, v must be [T, Hkv, d] matching q, with Hkv dividing H")
         if varlen_offsets.dtype != torch.int32:
             raise TypeError("varlen offsets must be int32")
         B = varlen_offsets.numel() - 1
@@ -163,6 +166,7 @@ def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_s
     opts.o_dtype = o_dtype
     opts.rescale_threshold = rescale_threshold
     opts.schedule = schedule
+    opts.kv_heads = Hkv
     st = fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets, stream, opts)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_ex")

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;   // 0.1.0
+constexpr int kVersion = 200;   // 0.2.0: grouped K/V heads
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -29,7 +29,8 @@ int check_args(const void *q, const void *k, const void *v, const void *o, const
         opts.rescale_threshold > 64.f)
         return FA_ERR_INVALID_ARG;
     if (opts.schedule < FA_SCHEDULE_AUTO || opts.schedule > FA_SCHEDULE_LPT) return FA_ERR_INVALID_ARG;
-    if (opts.reserved != 0) return FA_ERR_INVALID_ARG;
+    if (opts.kv_heads < 0 || opts.kv_heads > H || (opts.kv_heads > 0 && H % opts.kv_heads != 0))
+        return FA_ERR_INVALID_ARG;
     if (opts.o_dtype != FA_DTYPE_BF16 && opts.o_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (offsets) {
@@ -39,7 +40,9 @@ int check_args(const void *q, const void *k, const void *v, const void *o, const
     // Tile count and element offsets must fit the kernel's integer arithmetic.
     const int64_t num_m = ((int64_t)Nq + fa::kBlockM - 1) / fa::kBlockM;
     if ((int64_t)B * H * num_m >= (int64_t)1 << 31) return FA_ERR_INVALID_ARG;
-    if ((int64_t)H * d >= (int64_t)1 << 31) return FA_ERR_INVALID_ARG;
+    // Byte offsets inside a tile's buffer descriptors are 32-bit: a 256-row
+    // Q/O tile spans 256 * H * d * 2 bytes.
+    if ((int64_t)fa::kBlockM * H * d * 2 >= (int64_t)1 << 32) return FA_ERR_INVALID_ARG;
     if ((int64_t)B * Nq >= (int64_t)1 << 31 || (int64_t)B * Nk >= (int64_t)1 << 31)
         return FA_ERR_INVALID_ARG;
     return FA_OK;
@@ -54,7 +57,7 @@ void fa_fwd_opts_default(fa_fwd_opts *opts) {
     opts->o_dtype = FA_DTYPE_BF16;
     opts->rescale_threshold = 8.0f;
     opts->schedule = FA_SCHEDULE_AUTO;
-    opts->reserved = 0;
+    opts->kv_heads = 0;
 }
 
 int fa_fwd_check(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -84,6 +87,8 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
     p.offsets = varlen_offsets;
     p.B = B;
     p.H = H;
+    p.group = op.kv_heads > 0 ? H / op.kv_heads : 1;   // query heads per K/V head
+    p.Hkv = H / p.group;
     p.Nq = Nq;
     p.Nk = Nk;
     p.num_m = (Nq + fa::kBlockM - 1) / fa::kBlockM;

@@ -37,21 +37,24 @@
 //   (v_permlane32_swap), instead of the warp-quad shuffles of the pages.
 // * P stays in registers.  The S^T accumulator of a 32-key tile, converted to
 //   bf16, is directly the B operand (keys x queries) of O^T += V^T P^T for two
-//   16-key steps; V^T is stored in LDS with the matching key permutation
-//   (within each 16-key group, keys 4..7 and 8..11 trade places), so every
-//   MFMA operand is one 16-byte LDS read.
+//   16-key steps.  The V^T operand comes from the row-major V tile by
+//   ds_read_b64_tr_b16 transpose reads, two per MFMA.
 // * O^T accumulates in registers with one query per lane, so the conditional
 //   rescale multiplies a lane's own row by its own alpha; a wave skips the
 //   multiply when no lane needs it (ballot), the CDNA analog of FA4's
 //   per-warp any_sync test.
-// * K and V^T blocks are double-buffered in LDS; the next block's global loads
-//   are issued before the current block's MFMAs and written to the other
-//   buffer afterwards, one barrier per block.  Row strides are padded by 16
-//   bytes so the 16-byte operand reads of 16 lanes cover 64 distinct banks.
+// * Ping-pong between the two waves of a SIMD (see the schedule below): one
+//   wave issues its MFMAs (S_j and O += P_{j-1} V_{j-1}) while the other
+//   runs its softmax on the VALU; workgroup barriers separate the phases.
+// * K and V blocks are double-buffered in LDS, staged through registers with
+//   buffer loads (range-checked per block) one phase ahead.  Row strides are
+//   padded (K by 16 bytes, V by 32 bytes) so the 16-byte K reads and the
+//   transpose reads of 16 lanes spread over the 64 banks.
 // * Tiles are mapped XCD-aware: workgroups are dispatched round-robin over the
 //   8 XCDs, so XCD x is given a contiguous set of (batch, head) pairs and its
 //   L2 holds their K/V.  Causal and varlen tiles go longest first (LPT,
 //   "FlashAttention-4 (下)", section 6).
+
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -248,14 +251,17 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     const int qw0 = m0 + 32 * w;          // first query row of this wave
     const int qrow = qw0 + lq;            // query row of this lane
     const bool row_ok = qrow < Nq;
-    const int64_t tok = (int64_t)p.H * D; // elements between consecutive tokens
+    const int64_t tok = (int64_t)p.H * D; // elements between consecutive Q/O tokens
+    const int64_t tkv = (int64_t)p.Hkv * D;      // ... K/V tokens (grouped K/V heads)
     const unsigned tokb = (unsigned)(tok * 2);   // ... in bytes
+    const unsigned tkvb = (unsigned)(tkv * 2);
+    const int hkv = tc.h / p.group;       // the K/V head this query head reads
     const int causal_shift = Nk - Nq;     // bottom-right alignment
     const int wave_last_row = min(qw0 + 31, Nq - 1);
 
     const unsigned short *Qg = (const unsigned short *)p.q + (int64_t)tc.q_tok0 * tok + tc.h * D;
-    const unsigned short *Kg = (const unsigned short *)p.k + (int64_t)tc.k_tok0 * tok + tc.h * D;
-    const unsigned short *Vg = (const unsigned short *)p.v + (int64_t)tc.k_tok0 * tok + tc.h * D;
+    const unsigned short *Kg = (const unsigned short *)p.k + (int64_t)tc.k_tok0 * tkv + hkv * D;
+    const unsigned short *Vg = (const unsigned short *)p.v + (int64_t)tc.k_tok0 * tkv + hkv * D;
 
     // Number of K/V blocks this tile visits (fully masked blocks are never loaded).
     int nblocks = (Nk + T::BN - 1) / T::BN;
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     auto block_bytes = [&](int kb) -> unsigned {
         const int rem = Nk - kb * T::BN;
         if (kb >= nblocks || rem <= 0) return 0u;
-        return (unsigned)(min(rem, T::BN) - 1) * tokb + (unsigned)(D * 2);
+        return (unsigned)(min(rem, T::BN) - 1) * tkvb + (unsigned)(D * 2);
     };
     auto active = [&](int kb) -> bool {   // does this wave have a live key in block kb?
         return qw0 < Nq && (!CAUSAL || kb * T::BN <= wave_last_row + causal_shift);
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     for (int rr = 0; rr < KPT2; ++rr) {
         const int u = gtid + rr * 256;
         const int row = 32 * grp + u / (D / 8), cc = u % (D / 8);
-        k_voff[rr] = (unsigned)row * tokb + 16u * cc;
+        k_voff[rr] = (unsigned)row * tkvb + 16u * cc;
         k_lds[rr] = row * T::KS + 8 * cc;
     }
     int v_lds[KPT2];
@@ -347,12 +353,12 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     u32x4 vreg[KPT2];
 
     auto load_k = [&](int kb) {
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)kb * T::BN * tok, block_bytes(kb));
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)kb * T::BN * tkv, block_bytes(kb));
 #pragma unroll
         for (int rr = 0; rr < KPT2; ++rr) kreg[rr] = buffer_load16(rk, k_voff[rr]);
     };
     auto load_v = [&](int kb) {
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)kb * T::BN * tok, block_bytes(kb));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)kb * T::BN * tkv, block_bytes(kb));
 #pragma unroll
         for (int rr = 0; rr < KPT2; ++rr) vreg[rr] = buffer_load16(rv, k_voff[rr]);
     };
@@ -368,8 +374,8 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     // S^T = K Q^T for the BN keys of a block.
     f32x16 s[T::NKT];
     auto qk = [&](const unsigned short *Ks) {
-        constexpr int NR = T::NDS * T::NKT;
-        constexpr int AHEAD = NR < 8 ? NR : 8;
+        constexpr int NR = T::NDS * T::NKT;       // K fragment reads, one MFMA each
+        constexpr int AHEAD = NR < 8 ? NR : 8;    // reads in flight ahead of the MFMAs
         bf16x8 kf[T::NDS][T::NKT];
 #pragma unroll
         for (int ds = 0; ds < T::NDS; ++ds)
@@ -385,10 +391,13 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int kt = 0; kt < T::NKT; ++kt)
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ds][kt], qf[ds], s[kt], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+        // Keep AHEAD fragment reads in flight (left alone, the scheduler
+        // recycles one register pair and waits out the LDS latency for every
+        // pair of MFMAs): reads first, then one MFMA per further read.
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);     // LDS reads
 #pragma unroll
         for (int i = 0; i < NR - AHEAD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);

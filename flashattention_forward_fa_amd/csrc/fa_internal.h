@@ -23,6 +23,8 @@ struct FwdParams {
     float *lse;
     const int32_t *offsets;   // varlen: int32 [B+1]; nullptr for fixed length
     int B, H, Nq, Nk;         // varlen: Nq = Nk = upper bound of the lengths
+    int Hkv;                  // K/V heads (divides H)
+    int group;                // H / Hkv: query head h reads K/V head h / group
     int num_m;                // query tiles per (batch, head) (upper bound for varlen)
     int num_tiles;            // grid size
     int lpt;                  // 1: longest-first order

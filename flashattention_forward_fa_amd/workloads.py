@@ -16,6 +16,8 @@ Recipe (every draw is seeded, ``numpy.random.default_rng`` / PCG64):
 * Variable length: the sequence lengths are drawn first, as integers uniform on
   an inclusive range, then Q, K, V of shape [T, head, dim] with T = sum(L); the
   int32 cumulative offsets [0, L0, L0+L1, ...] describe the packing.
+* Grouped K/V heads: K and V are drawn with Hkv heads ([.., Hkv, dim]); with
+  Hkv = H the draws are the multi-head ones.
 
 The named workloads mirror the five synthetic configurations the method is
 measured on (seed = 1000 + number).
@@ -75,10 +77,15 @@ class Workload:
     offsets: Optional[np.ndarray] = None   # int32 [B+1] for packed varlen
     lengths: Optional[np.ndarray] = None
     notes: dict = field(default_factory=dict)
+    Hkv: Optional[int] = None        # K/V heads; None = H
 
     @property
     def varlen(self) -> bool:
         return self.offsets is not None
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
 
     @property
     def total_tokens(self) -> int:
@@ -97,15 +104,18 @@ class Workload:
         osz = 4 if self.o_dtype == "f32" else 2
         if self.varlen:
             T = self.total_tokens
-            return T * self.H * self.d * (3 * 2 + osz) + T * self.H * 4
+            return T * self.H * self.d * (2 + osz) + 2 * T * self.kv_heads * self.d * 2 \
+                + T * self.H * 4
         qo = self.B * self.Nq * self.H
-        kv = self.B * self.Nk * self.H
+        kv = self.B * self.Nk * self.kv_heads
         return qo * self.d * (2 + osz) + 2 * kv * self.d * 2 + qo * 4
 
     def describe(self) -> dict:
         dsc = dict(workload=self.name, batch=self.B, heads=self.H, seq_q=self.Nq, seq_k=self.Nk,
                    head_dim=self.d, causal=self.causal, scale=self.scale, o_dtype=self.o_dtype,
                    seed=self.seed)
+        if self.Hkv is not None and self.Hkv != self.H:
+            dsc.update(kv_heads=self.Hkv)
         if self.varlen:
             dsc.update(lengths=[int(x) for x in self.lengths], total_tokens=self.total_tokens)
         dsc.update(self.notes)
@@ -120,28 +130,32 @@ def _draw_qkv(rng, shape_q, shape_kv):
 
 
 def make_fixed(B, H, Nq, Nk, d, *, seed, causal, scale=None, o_dtype="bf16",
-               outlier_frac=0.0, outlier_scale=8.0, name=None) -> Workload:
-    """Fixed-length [B, N, H, d] inputs drawn i.i.d. N(0,1) and rounded to bf16."""
+               outlier_frac=0.0, outlier_scale=8.0, name=None, Hkv=None) -> Workload:
+    """Fixed-length inputs, q [B, Nq, H, d] and k, v [B, Nk, Hkv, d] (Hkv = H
+    unless given), drawn i.i.d. N(0,1) and rounded to bf16."""
     rng = np.random.default_rng(seed)
-    q, k, v = _draw_qkv(rng, (B, Nq, H, d), (B, Nk, H, d))
+    hk = H if Hkv is None else Hkv
+    q, k, v = _draw_qkv(rng, (B, Nq, H, d), (B, Nk, hk, d))
     notes = {}
     if outlier_frac > 0.0:
         n_out = int(round(outlier_frac * Nk))
         for b in range(B):
-            for h in range(H):
+            for h in range(hk):
                 pos = rng.choice(Nk, n_out, replace=False)
                 k[b, pos, h, :] *= np.float32(outlier_scale)
         notes = dict(outlier_rows_per_head=n_out, outlier_scale=outlier_scale)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    return Workload(name or f"B{B}_H{H}_Nq{Nq}_Nk{Nk}_d{d}_{'causal' if causal else 'full'}",
+    kvs = "" if Hkv is None or Hkv == H else f"_Hkv{Hkv}"
+    return Workload(name or f"B{B}_H{H}{kvs}_Nq{Nq}_Nk{Nk}_d{d}_{'causal' if causal else 'full'}",
                     B, H, Nq, Nk, d, bool(causal), float(scale), o_dtype, seed,
-                    bf16_bits(q), bf16_bits(k), bf16_bits(v), notes=notes)
+                    bf16_bits(q), bf16_bits(k), bf16_bits(v), notes=notes, Hkv=Hkv)
 
 
 def make_varlen(H, d, *, seed, causal=True, lengths=None, nseq=16, len_lo=128, len_hi=8192,
-                scale=None, o_dtype="bf16", name=None) -> Workload:
-    """Packed [T, H, d] inputs; lengths drawn uniform on [len_lo, len_hi] unless given."""
+                scale=None, o_dtype="bf16", name=None, Hkv=None) -> Workload:
+    """Packed inputs, q [T, H, d] and k, v [T, Hkv, d]; lengths drawn uniform on
+    [len_lo, len_hi] unless given."""
     rng = np.random.default_rng(seed)
     if lengths is None:
         lengths = rng.integers(len_lo, len_hi, nseq, endpoint=True)
@@ -149,14 +163,15 @@ def make_varlen(H, d, *, seed, causal=True, lengths=None, nseq=16, len_lo=128, l
     offsets = np.zeros(len(lengths) + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(lengths)
     T = int(offsets[-1])
-    q, k, v = _draw_qkv(rng, (T, H, d), (T, H, d))
+    hk = H if Hkv is None else Hkv
+    q, k, v = _draw_qkv(rng, (T, H, d), (T, hk, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     maxlen = int(lengths.max()) if len(lengths) else 0
     return Workload(name or f"varlen{len(lengths)}_H{H}_d{d}", len(lengths), H, maxlen, maxlen,
                     d, bool(causal), float(scale), o_dtype, seed,
                     bf16_bits(q), bf16_bits(k), bf16_bits(v),
-                    offsets=offsets.astype(np.int32), lengths=lengths)
+                    offsets=offsets.astype(np.int32), lengths=lengths, Hkv=Hkv)
 
 
 CONFIG_NAMES = {
@@ -188,3 +203,16 @@ def config(n: int) -> Workload:
         return make_varlen(32, 64, seed=seed, causal=True, nseq=16, len_lo=128, len_hi=8192,
                            scale=1.0 / 8.0, name=CONFIG_NAMES[5])
     raise ValueError(f"no configuration {n}")
+
+
+def grouped(n: int, kv_heads: int) -> Workload:
+    """A fixed-length configuration (2, 3 or 4) with K/V drawn for kv_heads heads
+    (grouped-query attention; same query shape, flops and seed)."""
+    base = {2: (4, 16, 2048, False, 0.0), 3: (2, 32, 4096, True, 0.0),
+            4: (1, 16, 16384, True, 0.01)}
+    if n not in base:
+        raise ValueError(f"no grouped variant of configuration {n}")
+    B, H, N, causal, frac = base[n]
+    return make_fixed(B, H, N, N, 128, seed=1000 + n, causal=causal, scale=1.0 / math.sqrt(128),
+                      outlier_frac=frac, outlier_scale=8.0, Hkv=kv_heads,
+                      name=f"{CONFIG_NAMES[n]}_Hkv{kv_heads}")

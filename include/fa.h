@@ -22,6 +22,11 @@
  * "Causal Mask"): query i may use keys j <= i + Nk - Nq.  A row with no usable
  * key gets O = 0 and LSE = -inf.
  *
+ * Grouped K/V heads (fa_fwd_ex, opts.kv_heads = Hkv; FA4 page, section "GQA
+ * support"): Hkv divides H and the G = H / Hkv consecutive query heads
+ * kv*G .. kv*G+G-1 share K/V head kv (Hkv = 1 is multi-query attention).
+ * fa_fwd, and kv_heads = 0, mean Hkv = H.
+ *
  * Conventions shared by every entry point:
  *   - q, k, v, o, lse and varlen_offsets are DEVICE pointers on the current
  *     HIP device; the caller owns them; libfa keeps no pointer after return.
@@ -32,20 +37,22 @@
  *   - Inputs are bf16 (raw 16-bit patterns).  O is bf16 by default (fp32 via
  *     fa_fwd_ex); LSE is fp32.
  *
- * Layouts (row-major, contiguous, head dimension fastest):
+ * Layouts (row-major, contiguous, head dimension fastest; Hkv = H unless
+ * opts.kv_heads says otherwise):
  *   fixed length (varlen_offsets == NULL):
- *     q [B, Nq, H, d], k and v [B, Nk, H, d], o [B, Nq, H, d], lse [B, H, Nq]
+ *     q [B, Nq, H, d], k and v [B, Nk, Hkv, d], o [B, Nq, H, d], lse [B, H, Nq]
  *   packed variable length (varlen_offsets != NULL):
  *     varlen_offsets: int32 [B + 1], offsets[0] = 0, non-decreasing; sequence
  *     b holds tokens offsets[b] .. offsets[b+1]-1 and attends to itself
  *     (self attention, Nq = Nk = its length).  With T = offsets[B]:
- *     q, k, v, o [T, H, d], lse [H, T].  Nq and Nk must both equal an upper
+ *     q, o [T, H, d], k, v [T, Hkv, d], lse [H, T].  Nq and Nk must both equal an upper
  *     bound of every sequence length (normally the maximum).  The device reads
  *     the offsets; they are not validated -- offsets that decrease, exceed T
  *     or a length above Nq are undefined behaviour.
  *
  * Supported: d in {64, 128}; B, H, Nq, Nk >= 1; any Nq, Nk (tails masked);
- * pointers 16-byte aligned; B*H*ceil(Nq/256) below 2^31.
+ * pointers 16-byte aligned; B*H*ceil(Nq/256) below 2^31; H*d below 2^23;
+ * B*Nq and B*Nk below 2^31.
  */
 #ifndef LIBFA_FA_H
 #define LIBFA_FA_H
@@ -85,16 +92,17 @@ typedef enum fa_schedule {
  *                       grows.  The upper bound keeps P <= 2^tau and the row
  *                       sum finite in fp32.
  *   schedule          : fa_schedule (default FA_SCHEDULE_AUTO).
- *   reserved          : must be 0.
+ *   kv_heads          : number of K/V heads Hkv; 0 (the default) means H,
+ *                       otherwise 1 <= Hkv <= H and Hkv divides H.
  */
 typedef struct fa_fwd_opts {
     int32_t o_dtype;
     float rescale_threshold;
     int32_t schedule;
-    int32_t reserved;
+    int32_t kv_heads;
 } fa_fwd_opts;
 
-/* Fill *opts with the defaults (bf16 O, tau = 8, automatic schedule). */
+/* Fill *opts with the defaults (bf16 O, tau = 8, automatic schedule, Hkv = H). */
 void fa_fwd_opts_default(fa_fwd_opts *opts);
 
 /*

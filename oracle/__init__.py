@@ -66,16 +66,18 @@ class Oracle:
         lib = ctypes.CDLL(lib_path)
         lib.oracle_attn_fwd.argtypes = [_F64P, _F64P, _F64P, _F64P, _F64P,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
-                                        ctypes.c_int]
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_fwd.restype = ctypes.c_int
         lib.oracle_attn_fwd_varlen.argtypes = [_F64P, _F64P, _F64P, _F64P, _F64P,
                                                ctypes.c_int64, _I64P, ctypes.c_int64,
-                                               ctypes.c_int64, ctypes.c_double, ctypes.c_int]
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                               ctypes.c_int]
         lib.oracle_attn_fwd_varlen.restype = ctypes.c_int
         lib.oracle_attn_fwd_rows.argtypes = [_F64P, _F64P, _F64P,
                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                             ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                             ctypes.c_int,
                                              _I64P, ctypes.c_int64, ctypes.c_int64, _I64P,
                                              _F64P, _F64P]
         lib.oracle_attn_fwd_rows.restype = ctypes.c_int
@@ -89,34 +91,40 @@ class Oracle:
         return int(self.lib.oracle_num_threads())
 
     def attention(self, q, k, v, scale: float, causal: bool):
-        """Fixed length: q [B,Nq,H,d], k/v [B,Nk,H,d] -> (o [B,Nq,H,d], lse [B,H,Nq])."""
+        """Fixed length: q [B,Nq,H,d], k/v [B,Nk,Hkv,d] (Hkv divides H)
+        -> (o [B,Nq,H,d], lse [B,H,Nq])."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         if q.ndim != 4 or k.shape != v.shape or k.ndim != 4:
-            raise ValueError("expected q [B,Nq,H,d] and k, v [B,Nk,H,d]")
+            raise ValueError("expected q [B,Nq,H,d] and k, v [B,Nk,Hkv,d]")
         B, Nq, H, d = q.shape
-        if k.shape[0] != B or k.shape[2] != H or k.shape[3] != d:
-            raise ValueError("q and k/v disagree on B, H or d")
+        Hkv = k.shape[2]
+        if k.shape[0] != B or k.shape[3] != d or Hkv < 1 or H % Hkv:
+            raise ValueError("q and k/v disagree on B or d, or Hkv does not divide H")
         Nk = k.shape[1]
         o = np.empty_like(q)
         lse = np.empty((B, H, Nq), dtype=np.float64)
-        rc = self.lib.oracle_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Nq, Nk, d,
+        rc = self.lib.oracle_attn_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, H, Hkv, Nq, Nk, d,
                                       float(scale), int(bool(causal)))
         if rc != 0:
             raise RuntimeError("oracle_attn_fwd failed")
         return o, lse
 
     def attention_varlen(self, q, k, v, offsets, scale: float, causal: bool):
-        """Packed varlen self attention: q/k/v [T,H,d], offsets [nseq+1] -> (o [T,H,d], lse [H,T])."""
+        """Packed varlen self attention: q [T,H,d], k/v [T,Hkv,d], offsets [nseq+1]
+        -> (o [T,H,d], lse [H,T])."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
         nseq = off.shape[0] - 1
         T, H, d = q.shape
+        Hkv = k.shape[1]
+        if k.shape != v.shape or k.shape[0] != T or k.shape[2] != d or Hkv < 1 or H % Hkv:
+            raise ValueError("expected k, v [T,Hkv,d] with Hkv dividing H")
         if off[0] != 0 or off[-1] != T or np.any(np.diff(off) < 0):
             raise ValueError("offsets must start at 0, be non-decreasing and end at T")
         o = np.empty_like(q)
         lse = np.empty((H, T), dtype=np.float64)
         rc = self.lib.oracle_attn_fwd_varlen(_p(q), _p(k), _p(v), _p(o), _p(lse), nseq,
-                                             _p(off, _I64P), H, d, float(scale),
+                                             _p(off, _I64P), H, Hkv, d, float(scale),
                                              int(bool(causal)))
         if rc != 0:
             raise RuntimeError("oracle_attn_fwd_varlen failed")
@@ -133,18 +141,21 @@ class Oracle:
         n = rows.shape[0]
         if offsets is None:
             _, Nq, H, d = q.shape
-            Nk = k.shape[1]
+            Nk, Hkv = k.shape[1], k.shape[2]
             if np.any(rows[:, 0] >= q.shape[0]):
                 raise ValueError("batch index out of range")
             off_p, nseq = None, 0
         else:
             off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
             _, H, d = q.shape
+            Hkv = k.shape[1]
             Nq = Nk = 0
             off_p, nseq = _p(off, _I64P), off.shape[0] - 1
         o = np.empty((n, d), dtype=np.float64)
         lse = np.empty((n,), dtype=np.float64)
-        rc = self.lib.oracle_attn_fwd_rows(_p(q), _p(k), _p(v), H, Nq, Nk, d, float(scale),
+        if Hkv < 1 or H % Hkv:
+            raise ValueError("Hkv must divide H")
+        rc = self.lib.oracle_attn_fwd_rows(_p(q), _p(k), _p(v), H, Hkv, Nq, Nk, d, float(scale),
                                            int(bool(causal)), off_p, nseq, n, _p(rows, _I64P),
                                            _p(o), _p(lse))
         if rc != 0:

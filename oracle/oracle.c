@@ -31,12 +31,17 @@
  * no valid key has O = 0 ("algorithm structure": O is 0 when the row sum is
  * 0) and LSE = -inf ("rescale and write-back": rows without a valid key).
  *
+ * Grouped K/V heads: "Flash Attention 4", section "GQA support": with H
+ * query heads and Hkv K/V heads (Hkv divides H), G = H / Hkv consecutive
+ * query heads share one K/V head, query head h = kv * G + offset, so query
+ * head h reads K/V head h / G.  Hkv = H is plain multi-head attention.
+ *
  * Layouts (all row-major, contiguous, fp64):
- *   fixed length : q [B, Nq, H, d]; k, v [B, Nk, H, d]; o [B, Nq, H, d];
+ *   fixed length : q [B, Nq, H, d]; k, v [B, Nk, Hkv, d]; o [B, Nq, H, d];
  *                  lse [B, H, Nq]
- *   packed varlen: q, k, v, o [T, H, d] with sequence b occupying tokens
- *                  offsets[b] .. offsets[b+1]-1 (self attention, Nq = Nk = L_b);
- *                  lse [H, T]
+ *   packed varlen: q, o [T, H, d]; k, v [T, Hkv, d] with sequence b occupying
+ *                  tokens offsets[b] .. offsets[b+1]-1 (self attention,
+ *                  Nq = Nk = L_b); lse [H, T]
  */
 #include <math.h>
 #include <stdint.h>
@@ -104,12 +109,14 @@ static void attention_row(const double *qi, const double *k, const double *v,
 /* Fixed-length batch, every row.  Returns 0, or -1 on bad arguments. */
 int oracle_attn_fwd(const double *q, const double *k, const double *v,
                     double *o, double *lse,
-                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                     double scale, int causal)
 {
-    if (!q || !k || !v || !o || !lse || B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0)
+    if (!q || !k || !v || !o || !lse || B < 0 || H < 0 || Nq < 0 || Nk < 0 || d <= 0 ||
+        Hkv <= 0 || H % Hkv != 0)
         return -1;
-    const int64_t stride = H * d;
+    const int64_t group = H / Hkv;      /* query heads per K/V head */
+    const int64_t stride = Hkv * d;     /* between consecutive keys */
     const int64_t nrows = B * H * Nq;
     int bad = 0;
 #pragma omp parallel
@@ -125,8 +132,8 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v,
                 int64_t h = (r / Nq) % H;
                 int64_t b = r / (Nq * H);
                 const double *qi = q + ((b * Nq + i) * H + h) * d;
-                const double *kb = k + (b * Nk * H + h) * d;
-                const double *vb = v + (b * Nk * H + h) * d;
+                const double *kb = k + (b * Nk * Hkv + h / group) * d;
+                const double *vb = v + (b * Nk * Hkv + h / group) * d;
                 attention_row(qi, kb, vb, stride, valid_keys(i, Nq, Nk, causal), d, scale,
                               s_buf, o + ((b * Nq + i) * H + h) * d,
                               lse + (b * H + h) * Nq + i);
@@ -140,10 +147,11 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v,
 /* Packed variable-length batch of nseq sequences, every row. */
 int oracle_attn_fwd_varlen(const double *q, const double *k, const double *v,
                            double *o, double *lse,
-                           int64_t nseq, const int64_t *offsets, int64_t H, int64_t d,
-                           double scale, int causal)
+                           int64_t nseq, const int64_t *offsets, int64_t H, int64_t Hkv,
+                           int64_t d, double scale, int causal)
 {
-    if (!q || !k || !v || !o || !lse || !offsets || nseq < 0 || H < 0 || d <= 0)
+    if (!q || !k || !v || !o || !lse || !offsets || nseq < 0 || H < 0 || d <= 0 ||
+        Hkv <= 0 || H % Hkv != 0)
         return -1;
     const int64_t T = offsets[nseq];
     int64_t maxlen = 0;
@@ -152,7 +160,8 @@ int oracle_attn_fwd_varlen(const double *q, const double *k, const double *v,
         if (L < 0) return -1;
         if (L > maxlen) maxlen = L;
     }
-    const int64_t stride = H * d;
+    const int64_t group = H / Hkv;
+    const int64_t stride = Hkv * d;
     int bad = 0;
 #pragma omp parallel
     {
@@ -170,8 +179,8 @@ int oracle_attn_fwd_varlen(const double *q, const double *k, const double *v,
                 int64_t start = offsets[b];
                 int64_t L = offsets[b + 1] - start;
                 int64_t i = t - start;
-                attention_row(q + (t * H + h) * d, k + (start * H + h) * d,
-                              v + (start * H + h) * d, stride,
+                attention_row(q + (t * H + h) * d, k + (start * Hkv + h / group) * d,
+                              v + (start * Hkv + h / group) * d, stride,
                               valid_keys(i, L, L, causal), d, scale, s_buf,
                               o + (t * H + h) * d, lse + h * T + t);
             }
@@ -188,13 +197,14 @@ int oracle_attn_fwd_varlen(const double *q, const double *k, const double *v,
  * position inside it.  Results go to o_out [nrows, d] and lse_out [nrows].
  */
 int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
-                         int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                         int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
                          double scale, int causal,
                          const int64_t *offsets, int64_t nseq,
                          int64_t nrows, const int64_t *rows,
                          double *o_out, double *lse_out)
 {
-    if (!q || !k || !v || !rows || !o_out || !lse_out || H <= 0 || d <= 0 || nrows < 0)
+    if (!q || !k || !v || !rows || !o_out || !lse_out || H <= 0 || d <= 0 || nrows < 0 ||
+        Hkv <= 0 || H % Hkv != 0)
         return -1;
     int64_t maxkeys = Nk;
     if (offsets) {
@@ -204,7 +214,8 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
             if (L > maxkeys) maxkeys = L;
         }
     }
-    const int64_t stride = H * d;
+    const int64_t group = H / Hkv;
+    const int64_t stride = Hkv * d;
     int bad = 0;
 #pragma omp parallel
     {
@@ -231,8 +242,8 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
                         continue;
                     }
                     qi = q + ((start + i) * H + h) * d;
-                    kb = k + (start * H + h) * d;
-                    vb = v + (start * H + h) * d;
+                    kb = k + (start * Hkv + h / group) * d;
+                    vb = v + (start * Hkv + h / group) * d;
                     nvalid = valid_keys(i, L, L, causal);
                 } else {
                     if (h < 0 || h >= H || i < 0 || i >= Nq || b < 0) {
@@ -241,8 +252,8 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
                         continue;
                     }
                     qi = q + ((b * Nq + i) * H + h) * d;
-                    kb = k + (b * Nk * H + h) * d;
-                    vb = v + (b * Nk * H + h) * d;
+                    kb = k + (b * Nk * Hkv + h / group) * d;
+                    vb = v + (b * Nk * Hkv + h / group) * d;
                     nvalid = valid_keys(i, Nq, Nk, causal);
                 }
                 attention_row(qi, kb, vb, stride, nvalid, d, scale, s_buf,

@@ -107,10 +107,13 @@ def pin_exercise7_bounds(orc):
 # ------------------------------------------------------------ library routine
 
 def _torch_reference(q, k, v, scale, causal):
+    """torch's fp64 CPU SDPA (its own grouped-head handling when k/v have fewer
+    heads) and scipy's logsumexp over explicitly repeated key heads."""
     import torch
     import torch.nn.functional as F
     from scipy.special import logsumexp
     Nq, Nk = q.shape[1], k.shape[1]
+    H, Hkv = q.shape[2], k.shape[2]
     tq = torch.from_numpy(q).permute(0, 2, 1, 3).contiguous()   # [B,H,N,d]
     tk = torch.from_numpy(k).permute(0, 2, 1, 3).contiguous()
     tv = torch.from_numpy(v).permute(0, 2, 1, 3).contiguous()
@@ -119,9 +122,11 @@ def _torch_reference(q, k, v, scale, causal):
     if causal:
         allowed = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)
         mask = torch.from_numpy(allowed)
-    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale,
+                                       enable_gqa=(H != Hkv))
     o = o.permute(0, 2, 1, 3).numpy()
-    s = scale * np.einsum("bqhd,bkhd->bhqk", q, k)
+    kr = np.repeat(k, H // Hkv, axis=2)
+    s = scale * np.einsum("bqhd,bkhd->bhqk", q, kr)
     s = np.where(allowed[None, None], s, -np.inf)
     lse = logsumexp(s, axis=-1)
     return o, lse
@@ -141,6 +146,89 @@ def pin_torch_sdpa(orc):
         ro, rlse = _torch_reference(q, k, v, scale, causal)
         _close(o, ro, tol=1e-12, what=f"O {B, H, Nq, Nk, d, causal}")
         _close(lse, rlse, tol=1e-12, what=f"LSE {B, H, Nq, Nk, d, causal}")
+
+
+def pin_torch_sdpa_grouped_heads(orc):
+    """Grouped K/V heads (Hkv < H, MQA at Hkv = 1) vs torch's SDPA with enable_gqa."""
+    rng = np.random.default_rng(8)
+    shapes = [(2, 4, 2, 5, 7, 4, False), (1, 6, 3, 9, 9, 8, True), (2, 4, 1, 6, 11, 5, True),
+              (1, 8, 2, 13, 6, 3, False)]
+    for (B, H, Hkv, Nq, Nk, d, causal) in shapes:
+        q = rng.standard_normal((B, Nq, H, d))
+        k = rng.standard_normal((B, Nk, Hkv, d))
+        v = rng.standard_normal((B, Nk, Hkv, d))
+        o, lse = orc.attention(q, k, v, 0.41, causal)
+        ro, rlse = _torch_reference(q, k, v, 0.41, causal)
+        _close(o, ro, tol=1e-12, what=f"O {B, H, Hkv, Nq, Nk, d, causal}")
+        _close(lse, rlse, tol=1e-12, what=f"LSE {B, H, Hkv, Nq, Nk, d, causal}")
+
+
+def load_gqa_exercise():
+    with open(os.path.join(GOLDEN, "gqa_exercise8.json")) as f:
+        return json.load(f)
+
+
+def pin_gqa_exercise8(orc):
+    """The page's head grouping (exercise 8: 32 query heads, 8 K/V heads): query
+    heads kv*G .. kv*G+G-1 read K/V head kv.  Each K/V head c carries V = c + 1
+    and K = 0 (uniform weights), so O of query head h is 1 + (the K/V head it read)."""
+    g = load_gqa_exercise()
+    H, Hkv = g["num_qo_heads"], g["num_kv_heads"]
+    G = g["GQA_RATIO"]
+    assert H // Hkv == G and g["BLK_M"] // G == g["SEQ_Q_PER_TILE"]
+    N, d = 3, 2
+    q = np.ones((1, N, H, d))
+    k = np.zeros((1, N, Hkv, d))
+    v = np.broadcast_to((np.arange(Hkv, dtype=np.float64) + 1.0)[None, None, :, None],
+                        (1, N, Hkv, d)).copy()
+    for causal in (False, True):
+        o, _ = orc.attention(q, k, v, 0.5, causal)
+        kv_read = o[0, :, :, 0] - 1.0                 # [N, H]
+        for row, (seq, head) in g["packed_rows"].items():
+            row = int(row)
+            assert row // G == seq and g["kv_head_idx"] * G + row % G == head
+            _close(kv_read[:, head], np.full(N, g["kv_head_idx"]), what=f"head {head}")
+        _close(kv_read, np.broadcast_to(np.arange(H) // G, (N, H)), what="all heads")
+        # varlen layout, same grouping
+        ov, _ = orc.attention_varlen(q[0], k[0], v[0], [0, N], 0.5, causal)
+        _close(ov[:, :, 0] - 1.0, np.broadcast_to(np.arange(H) // G, (N, H)), what="varlen heads")
+
+
+def pin_gqa_equals_repeated_heads(orc):
+    """Grouped K/V heads give exactly the multi-head result on K/V with each head
+    repeated G times consecutively (fixed, varlen and selected rows)."""
+    rng = np.random.default_rng(9)
+    B, H, Hkv, Nq, Nk, d = 2, 6, 2, 5, 8, 4
+    q = rng.standard_normal((B, Nq, H, d))
+    k = rng.standard_normal((B, Nk, Hkv, d))
+    v = rng.standard_normal((B, Nk, Hkv, d))
+    kr, vr = np.repeat(k, H // Hkv, axis=2), np.repeat(v, H // Hkv, axis=2)
+    for causal in (False, True):
+        o, lse = orc.attention(q, k, v, 0.55, causal)
+        o1, l1 = orc.attention(q, kr, vr, 0.55, causal)
+        _close(o, o1, what="O")
+        _close(lse, l1, what="LSE")
+        rows = np.array([[0, 5, 4], [1, 2, 0], [1, 3, 2]])
+        ro, rl = orc.attention_rows(q, k, v, 0.55, causal, rows)
+        for n, (b, h, i) in enumerate(rows):
+            _close(ro[n], o[b, i, h], what=f"row {n}")
+            _close(rl[n], lse[b, h, i], what=f"lse {n}")
+    lengths = [3, 6]
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    T = off[-1]
+    q = rng.standard_normal((T, H, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    kr, vr = np.repeat(k, H // Hkv, axis=1), np.repeat(v, H // Hkv, axis=1)
+    o, lse = orc.attention_varlen(q, k, v, off, 0.55, True)
+    o1, l1 = orc.attention_varlen(q, kr, vr, off, 0.55, True)
+    _close(o, o1, what="varlen O")
+    _close(lse, l1, what="varlen LSE")
+    rows = np.array([[1, 4, 5], [0, 1, 2]])
+    ro, rl = orc.attention_rows(q, k, v, 0.55, True, rows, offsets=off)
+    for n, (b, h, i) in enumerate(rows):
+        _close(ro[n], o[off[b] + i, h], what=f"varlen row {n}")
+        _close(rl[n], lse[h, off[b] + i], what=f"varlen lse {n}")
 
 
 # ------------------------------------------------------------ invariants
@@ -331,4 +419,5 @@ ALL_PINS = [pin_worked_example, pin_causal_figure12, pin_bottom_right_alignment,
             pin_exercise7_bounds, pin_torch_sdpa, pin_rows_sum_to_one, pin_shift_invariance,
             pin_causal_row0, pin_convex_hull, pin_future_independence, pin_scale_zero_mean,
             pin_rows_without_keys, pin_key_permutation, pin_head_batch_slices,
-            pin_varlen_is_per_sequence, pin_rows_match_full]
+            pin_varlen_is_per_sequence, pin_rows_match_full, pin_torch_sdpa_grouped_heads,
+            pin_gqa_exercise8, pin_gqa_equals_repeated_heads]

@@ -32,7 +32,7 @@ def test_exports_every_declared_function():
 def test_version_and_defaults():
     assert fa.fa_version() >= 100
     o = fa.fa_fwd_opts_default()
-    assert (o.o_dtype, o.rescale_threshold, o.schedule, o.reserved) == (0, 8.0, 0, 0)
+    assert (o.o_dtype, o.rescale_threshold, o.schedule, o.kv_heads) == (0, 8.0, 0, 0)
 
 
 def test_status_strings():
@@ -93,7 +93,14 @@ def test_bad_threshold(tau):
 def test_bad_options():
     assert check(opts=opts(o_dtype=7)) == fa.FA_ERR_UNSUPPORTED
     assert check(opts=opts(schedule=3)) == fa.FA_ERR_INVALID_ARG
-    assert check(opts=opts(reserved=1)) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("H,kv,status", [(8, 0, 0), (8, 8, 0), (8, 4, 0), (8, 2, 0), (8, 1, 0),
+                                         (8, 3, -1), (8, 16, -1), (8, -1, -1), (6, 4, -1),
+                                         (6, 3, 0)])
+def test_kv_heads(H, kv, status):
+    """Grouped K/V heads: 0 (= H) or a divisor of H."""
+    assert check(H=H, opts=opts(kv_heads=kv)) == status
 
 
 def test_varlen_rules():
@@ -103,6 +110,9 @@ def test_varlen_rules():
 
 def test_size_overflow_rejected():
     assert check(B=1 << 20, H=1 << 10, Nq=1 << 16, Nk=16) == fa.FA_ERR_INVALID_ARG
+    # a 256-row tile's byte offsets must fit 32 bits: H*d < 2^23
+    assert check(H=1 << 16, d=128) == fa.FA_ERR_INVALID_ARG
+    assert check(H=(1 << 16) - 1, d=128) == fa.FA_OK
 
 
 def test_rejected_launch_makes_no_hip_call():

@@ -178,6 +178,67 @@ def test_outputs_stay_in_bounds():
     assert np.all(np.isfinite(ob[pad:pad + n_o]))
 
 
+# ------------------------------------------------------------ grouped K/V heads
+
+GROUPED = [
+    # B, H, Hkv, Nq, Nk, d, causal
+    (2, 8, 2, 300, 300, 128, True),
+    (1, 6, 3, 200, 333, 64, False),
+    (1, 4, 1, 257, 257, 128, True),    # one K/V head (multi-query)
+    (2, 8, 4, 100, 700, 64, True),     # Nq < Nk
+]
+
+
+@pytest.mark.parametrize("tau", [8.0, 0.0])
+@pytest.mark.parametrize("shape", GROUPED, ids=lambda s: "B{}H{}kv{}q{}k{}d{}{}".format(*s[:6], "c" if s[6] else "f"))
+def test_grouped_heads_full(shape, tau):
+    B, H, Hkv, Nq, Nk, d, causal = shape
+    w = wl.make_fixed(B, H, Nq, Nk, d, seed=H * 100 + Hkv + Nq, causal=causal, Hkv=Hkv)
+    _full_check(w, tau)
+    _full_check(w, tau, o_dtype=1, what=w.name + "/f32out")
+
+
+def test_grouped_heads_varlen():
+    w = wl.make_varlen(8, 64, seed=51, lengths=[300, 1, 129, 513], causal=True, Hkv=2)
+    _full_check(w, 8.0)
+    _full_check(w, 0.0)
+    w = wl.make_varlen(4, 128, seed=52, lengths=[77, 256], causal=False, Hkv=1)
+    _full_check(w, 8.0, o_dtype=1)
+
+
+def test_grouped_equals_repeated_heads():
+    """Grouped K/V heads give, bit for bit, what the same call gives on K/V with
+    each head repeated G times consecutively (fixed length and varlen)."""
+    import torch
+    import flashattention_forward_fa_amd as fa
+    for w in (wl.make_fixed(2, 8, 333, 333, 128, seed=53, causal=True, Hkv=2),
+              wl.make_varlen(6, 64, seed=54, lengths=[200, 513, 3], causal=True, Hkv=3)):
+        q, k, v, off = parity.to_device(w)
+        G = w.H // w.kv_heads
+        ax = 1 if w.varlen else 2
+        kr = k.repeat_interleave(G, dim=ax).contiguous()
+        vr = v.repeat_interleave(G, dim=ax).contiguous()
+        ms = w.Nq if w.varlen else None
+        o1, l1 = fa.attention(q, k, v, w.scale, w.causal, varlen_offsets=off, max_seqlen=ms)
+        o2, l2 = fa.attention(q, kr, vr, w.scale, w.causal, varlen_offsets=off, max_seqlen=ms)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), w.name
+
+
+@pytest.mark.parametrize("tau", [8.0, 0.0])
+def test_grouped_full_size(tau):
+    """The causal B=2, H=32, N=4096, d=128 workload with 8 K/V heads, sampled rows."""
+    w = wl.grouped(3, 8)
+    rows = parity.sample_rows(w, n_random=256, seed=77)
+    q, k, v = parity.inputs_f64(w)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, w.causal, rows)
+    del q, k, v
+    o, lse = parity.run_gpu(w, tau=tau)
+    go, gl = parity.gather_rows(w, o, lse, rows)
+    stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=True, what=f"{w.name} tau={tau}")
+    print(f"{w.name} tau={tau}: {len(rows)} rows {stats}")
+
+
 # ------------------------------------------------------------ the five configurations
 
 _cache = {}

@@ -1,7 +1,7 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU) and check that
 the pins catch every one of them.  This shows the pins constrain each part of
 the oracle: the scale, the maximum subtraction, the normaliser, the key/value
-strides, the mask alignment and the LSE."""
+strides, the K/V head of each query head, the mask alignment and the LSE."""
 import os
 import subprocess
 
@@ -22,8 +22,14 @@ MUTANTS = {
     "top_left_alignment": ("int64_t last = i + Nk - Nq;", "int64_t last = i;"),
     "lse_without_max": ("*lse = m + log(l);", "*lse = log(l);"),
     "empty_row_lse_zero": ("*lse = -INFINITY;", "*lse = 0.0;"),
-    "key_head_offset_dropped": ("const double *kb = k + (b * Nk * H + h) * d;",
-                                "const double *kb = k + (b * Nk * H) * d;"),
+    "key_head_offset_dropped": ("const double *kb = k + (b * Nk * Hkv + h / group) * d;",
+                                "const double *kb = k + (b * Nk * Hkv) * d;"),
+    "kv_head_modulo": ("const double *kb = k + (b * Nk * Hkv + h / group) * d;\n"
+                       "                const double *vb = v + (b * Nk * Hkv + h / group) * d;",
+                       "const double *kb = k + (b * Nk * Hkv + h % Hkv) * d;\n"
+                       "                const double *vb = v + (b * Nk * Hkv + h % Hkv) * d;"),
+    "kv_stride_query_heads": ("const int64_t stride = Hkv * d;     /* between consecutive keys */",
+                              "const int64_t stride = H * d;     /* between consecutive keys */"),
     "lse_wrong_slot": ("lse + (b * H + h) * Nq + i);", "lse + (h * B + b) * Nq + i);"),
 }
 
