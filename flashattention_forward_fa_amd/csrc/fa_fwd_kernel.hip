@@ -47,9 +47,9 @@
 //   wave issues its MFMAs (S_j and O += P_{j-1} V_{j-1}) while the other
 //   runs its softmax on the VALU; workgroup barriers separate the phases.
 // * K and V blocks are double-buffered in LDS, staged through registers with
-//   buffer loads (range-checked per block) one phase ahead.  Row strides are
-//   padded (K by 16 bytes, V by 32 bytes) so the 16-byte K reads and the
-//   transpose reads of 16 lanes spread over the 64 banks.
+//   buffer loads (range-checked per block) one phase ahead.  K rows are
+//   padded by 16 bytes and V rows swizzled (chunk c of row r at c ^ f(r)), so
+//   the 16-byte K reads and the transpose reads meet no bank conflict.
 // * Tiles are mapped XCD-aware: workgroups are dispatched round-robin over the
 //   8 XCDs, so XCD x is given a contiguous set of (batch, head) pairs and its
 //   L2 holds their K/V.  Causal and varlen tiles go longest first (LPT,
@@ -82,9 +82,8 @@ struct Tile {
     static constexpr int BM = kBlockM;
     static constexpr int NT = 64 * NW;        // threads per workgroup
     static constexpr int KS = D + 8;          // K row stride in LDS (bf16 elements)
-    static constexpr int VS = D + 16;         // V row stride in LDS (transpose reads)
     static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = BN * VS;
+    static constexpr int V_ELEMS = BN * D;    // V rows unpadded, 16-byte chunks swizzled
     static constexpr int LDS_BYTES = (2 * K_ELEMS + 2 * V_ELEMS) * 2;
     static constexpr int NKT = BN / 32;       // 32-key tiles of S^T per block
     static constexpr int NDS = D / 16;        // 16-wide head-dim steps of S^T
@@ -95,6 +94,19 @@ struct Tile {
     static_assert(KCH % NT == 0, "K block must split evenly over the threads");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
+
+// V tile layout in LDS: row r (a key) holds its D values as 16-byte chunks,
+// chunk c stored at position c ^ vswz<D>(r).  A transpose read serves 32
+// lanes at once: lanes 0-31 read rows 4g+0..3 (+8, +16 ks) at four chunks
+// 4dt..4dt+3, and the swizzle puts those four rows on disjoint banks
+// (rows of 256 B at D = 128 start on bank 0, so each row gets its own
+// quarter; rows of 128 B at D = 64 pair up on a bank base, so rows r and
+// r + 2 take opposite halves).  16-byte writes are conflict-free either way.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) ^ ((r >> 2) & 3);
+    else return ((r >> 1) & 1) << 2;
+}
 
 __device__ __forceinline__ float lane_pair_max(float x) {
     // Combine lanes l and l^32 (both halves see the maximum of the pair).
@@ -346,7 +358,8 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int rr = 0; rr < KPT2; ++rr) {
         const int u = gtid + rr * 256;
-        v_lds[rr] = (32 * grp + u / (D / 8)) * T::VS + 8 * (u % (D / 8));
+        const int row = 32 * grp + u / (D / 8);
+        v_lds[rr] = row * D + (((u % (D / 8)) ^ vswz<D>(row)) << 3);
     }
 
     u32x4 kreg[KPT2];
@@ -419,15 +432,26 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     // ds_read_b64_tr_b16 returns to lane i, element e, V[row + e][col + i].
     // Two reads give slots 0-3 (keys 4g..4g+3) and 4-7 (keys 8+4g..8+4g+3)
     // of the 16-key step, the key order of the P^T operand.
-    const int tr_off = (4 * g + ((lane & 15) >> 2)) * T::VS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // Offsets (elements) of this lane's transpose reads for each 32-wide
+    // head-dim tile dt and key half h; key step ks adds 16 rows, which leaves
+    // the swizzle unchanged.
+    int v_off[T::NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < T::NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 4 * g + ((lane & 15) >> 2) + 8 * h;
+            const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            v_off[dt][h] = row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
+        }
     auto pv = [&](const unsigned short *Vs) {
 #pragma unroll
         for (int ks = 0; ks < T::NKS; ++ks) {
 #pragma unroll
             for (int dt = 0; dt < T::NDT; ++dt) {
-                const unsigned short *a0 = Vs + tr_off + 16 * ks * T::VS + 32 * dt;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)a0);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + 8 * T::VS));
+                const unsigned short *a0 = Vs + 16 * ks * D;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][0]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][1]));
                 const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[dt], 0, 0, 0);
