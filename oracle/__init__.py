@@ -81,6 +81,13 @@ class Oracle:
                                              _I64P, ctypes.c_int64, ctypes.c_int64, _I64P,
                                              _F64P, _F64P]
         lib.oracle_attn_fwd_rows.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [_F64P] * 7 + [ctypes.c_int64] * 6 + [ctypes.c_double,
+                                                                             ctypes.c_int]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_bwd_varlen.argtypes = [_F64P] * 7 + [ctypes.c_int64, _I64P, ctypes.c_int64,
+                                                             ctypes.c_int64, ctypes.c_int64,
+                                                             ctypes.c_double, ctypes.c_int]
+        lib.oracle_attn_bwd_varlen.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -163,6 +170,43 @@ class Oracle:
         return o, lse
 
 
+    def attention_bwd(self, q, k, v, dout, scale: float, causal: bool):
+        """Gradients of O in Q, K, V for the upstream gradient dout (shaped like O).
+
+        Fixed length: q, dout [B,Nq,H,d], k, v [B,Nk,Hkv,d] -> (dq, dk, dv)."""
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or dout.shape != q.shape:
+            raise ValueError("expected q, dout [B,Nq,H,d] and k, v [B,Nk,Hkv,d]")
+        B, Nq, H, d = q.shape
+        Nk, Hkv = k.shape[1], k.shape[2]
+        if k.shape[0] != B or k.shape[3] != d or Hkv < 1 or H % Hkv:
+            raise ValueError("q and k/v disagree on B or d, or Hkv does not divide H")
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        rc = self.lib.oracle_attn_bwd(_p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv),
+                                      B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)))
+        if rc != 0:
+            raise RuntimeError("oracle_attn_bwd failed")
+        return dq, dk, dv
+
+    def attention_bwd_varlen(self, q, k, v, dout, offsets, scale: float, causal: bool):
+        """Packed varlen gradients: q, dout [T,H,d], k, v [T,Hkv,d] -> (dq, dk, dv)."""
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        off = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        T, H, d = q.shape
+        Hkv = k.shape[1]
+        if k.shape != v.shape or k.shape[0] != T or dout.shape != q.shape or Hkv < 1 or H % Hkv:
+            raise ValueError("expected q, dout [T,H,d] and k, v [T,Hkv,d]")
+        if off[0] != 0 or off[-1] != T or np.any(np.diff(off) < 0):
+            raise ValueError("offsets must start at 0, be non-decreasing and end at T")
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        rc = self.lib.oracle_attn_bwd_varlen(_p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk),
+                                             _p(dv), off.shape[0] - 1, _p(off, _I64P), H, Hkv, d,
+                                             float(scale), int(bool(causal)))
+        if rc != 0:
+            raise RuntimeError("oracle_attn_bwd_varlen failed")
+        return dq, dk, dv
+
+
 def default() -> Oracle:
     """The oracle built from oracle.c in this directory (built on first use)."""
     global _default
@@ -181,3 +225,11 @@ def attention_varlen(q, k, v, offsets, scale: float, causal: bool):
 
 def attention_rows(q, k, v, scale: float, causal: bool, rows, offsets=None):
     return default().attention_rows(q, k, v, scale, causal, rows, offsets)
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool):
+    return default().attention_bwd(q, k, v, dout, scale, causal)
+
+
+def attention_bwd_varlen(q, k, v, dout, offsets, scale: float, causal: bool):
+    return default().attention_bwd_varlen(q, k, v, dout, offsets, scale, causal)

@@ -264,3 +264,151 @@ int oracle_attn_fwd_rows(const double *q, const double *k, const double *v,
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Backward pass (gradients of O with respect to Q, K, V).
+ *
+ * "FlashAttention-4（下）" (argus-lessons), section 1: the backward recomputes
+ * S and P and takes the gradients of the two products, dP and dV for O = PV,
+ * dQ = dS K and dK = dS^T Q for S = Q K^T (scaled), with dS the gradient of
+ * the row softmax.  Written out for one (batch, head), valid keys j of row i:
+ *
+ *   s_ij  = scale * (q_i . k_j),  LSE_i = ln sum_j exp(s_ij),  P_ij = exp(s_ij - LSE_i)
+ *   dV_j  = sum_i P_ij dO_i                      (gradient of O = P V in V)
+ *   dP_ij = dO_i . v_j                           (... in P)
+ *   D_i   = sum_j P_ij dP_ij                     (= dO_i . O_i)
+ *   dS_ij = P_ij (dP_ij - D_i)                   (row-softmax Jacobian applied to dP)
+ *   dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
+ *
+ * With grouped K/V heads the G query heads of a K/V head add into its dK, dV.
+ * Rows without a valid key contribute nothing.  Everything is recomputed here
+ * in fp64 from q, k, v, dO (the forward's O and LSE are not inputs).
+ * Layouts as for the forward; dq like q, dk and dv like k.
+ */
+static void bwd_head(const double *q, const double *k, const double *v, const double *dout,
+                     double *dq, double *dk, double *dv,
+                     int64_t qstride, int64_t kstride, int64_t Nq, int64_t Nk, int64_t d,
+                     double scale, int causal, double *p_buf, double *dp_buf)
+{
+    /* q, dout, dq: query rows at qstride; k, v, dk, dv: key rows at kstride */
+    for (int64_t i = 0; i < Nq; ++i) {
+        const int64_t nvalid = valid_keys(i, Nq, Nk, causal);
+        if (nvalid <= 0) continue;
+        const double *qi = q + i * qstride;
+        const double *doi = dout + i * qstride;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < nvalid; ++j) {
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += qi[c] * k[j * kstride + c];
+            p_buf[j] = scale * dot;
+            if (p_buf[j] > m) m = p_buf[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < nvalid; ++j) l += exp(p_buf[j] - m);
+        const double lse = m + log(l);
+        double D = 0.0;
+        for (int64_t j = 0; j < nvalid; ++j) {
+            p_buf[j] = exp(p_buf[j] - lse);
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c) dot += doi[c] * v[j * kstride + c];
+            dp_buf[j] = dot;
+            D += p_buf[j] * dot;
+        }
+        double *dqi = dq + i * qstride;
+        for (int64_t j = 0; j < nvalid; ++j) {
+            const double ds = p_buf[j] * (dp_buf[j] - D);
+            for (int64_t c = 0; c < d; ++c) {
+                dqi[c] += scale * ds * k[j * kstride + c];
+                dk[j * kstride + c] += scale * ds * qi[c];
+                dv[j * kstride + c] += p_buf[j] * doi[c];
+            }
+        }
+    }
+}
+
+/* Fixed length, every gradient.  dq, dk, dv are overwritten. */
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv,
+                    int64_t B, int64_t H, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t d,
+                    double scale, int causal)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B < 0 || H < 0 || Nq < 0 || Nk < 0 ||
+        d <= 0 || Hkv <= 0 || H % Hkv != 0)
+        return -1;
+    const int64_t group = H / Hkv;
+    memset(dq, 0, sizeof(double) * (size_t)(B * Nq * H * d));
+    memset(dk, 0, sizeof(double) * (size_t)(B * Nk * Hkv * d));
+    memset(dv, 0, sizeof(double) * (size_t)(B * Nk * Hkv * d));
+    int bad = 0;
+    /* one (batch, K/V head) per iteration: its query heads are the only writers of its dK, dV */
+#pragma omp parallel
+    {
+        double *p_buf = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        double *dp_buf = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        if (!p_buf || !dp_buf) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < B * Hkv; ++u) {
+                const int64_t b = u / Hkv, kvh = u % Hkv;
+                for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)
+                    bwd_head(q + (b * Nq * H + h) * d, k + (b * Nk * Hkv + kvh) * d,
+                             v + (b * Nk * Hkv + kvh) * d, dout + (b * Nq * H + h) * d,
+                             dq + (b * Nq * H + h) * d, dk + (b * Nk * Hkv + kvh) * d,
+                             dv + (b * Nk * Hkv + kvh) * d, H * d, Hkv * d, Nq, Nk, d,
+                             scale, causal, p_buf, dp_buf);
+            }
+        }
+        free(p_buf);
+        free(dp_buf);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Packed variable length (self attention per sequence), every gradient. */
+int oracle_attn_bwd_varlen(const double *q, const double *k, const double *v, const double *dout,
+                           double *dq, double *dk, double *dv,
+                           int64_t nseq, const int64_t *offsets, int64_t H, int64_t Hkv,
+                           int64_t d, double scale, int causal)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || !offsets || nseq < 0 || H < 0 ||
+        d <= 0 || Hkv <= 0 || H % Hkv != 0)
+        return -1;
+    const int64_t T = offsets[nseq];
+    int64_t maxlen = 0;
+    for (int64_t b = 0; b < nseq; ++b) {
+        int64_t L = offsets[b + 1] - offsets[b];
+        if (L < 0) return -1;
+        if (L > maxlen) maxlen = L;
+    }
+    const int64_t group = H / Hkv;
+    memset(dq, 0, sizeof(double) * (size_t)(T * H * d));
+    memset(dk, 0, sizeof(double) * (size_t)(T * Hkv * d));
+    memset(dv, 0, sizeof(double) * (size_t)(T * Hkv * d));
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *p_buf = (double *)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1));
+        double *dp_buf = (double *)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1));
+        if (!p_buf || !dp_buf) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t u = 0; u < nseq * Hkv; ++u) {
+                const int64_t b = u / Hkv, kvh = u % Hkv;
+                const int64_t start = offsets[b], L = offsets[b + 1] - start;
+                for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)
+                    bwd_head(q + (start * H + h) * d, k + (start * Hkv + kvh) * d,
+                             v + (start * Hkv + kvh) * d, dout + (start * H + h) * d,
+                             dq + (start * H + h) * d, dk + (start * Hkv + kvh) * d,
+                             dv + (start * Hkv + kvh) * d, H * d, Hkv * d, L, L, d,
+                             scale, causal, p_buf, dp_buf);
+            }
+        }
+        free(p_buf);
+        free(dp_buf);
+    }
+    return bad ? -1 : 0;
+}

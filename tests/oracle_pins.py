@@ -415,9 +415,126 @@ def pin_rows_match_full(orc):
         _close(rl[n], lse[h, off[b] + i], what=f"varlen lse {n}")
 
 
+# ------------------------------------------------------------ backward
+
+def _torch_grads(q, k, v, dout, scale, causal):
+    """Gradients from torch's fp64 CPU autograd through its SDPA (a library routine)."""
+    import torch
+    import torch.nn.functional as F
+    Nq, Nk = q.shape[1], k.shape[1]
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3).contiguous().requires_grad_()
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).contiguous().requires_grad_()
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).contiguous().requires_grad_()
+    mask = None
+    if causal:
+        mask = torch.from_numpy(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq))
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale,
+                                       enable_gqa=(q.shape[2] != k.shape[2]))
+    o.backward(torch.from_numpy(dout).permute(0, 2, 1, 3).contiguous())
+    return tuple(t.grad.permute(0, 2, 1, 3).numpy() for t in (tq, tk, tv))
+
+
+def pin_bwd_torch_autograd(orc):
+    """dQ, dK, dV vs torch's fp64 autograd of SDPA (grouped heads, Nq != Nk, causal)."""
+    rng = np.random.default_rng(30)
+    shapes = [(2, 3, 3, 5, 7, 4, False), (1, 4, 2, 9, 9, 8, True), (2, 4, 1, 6, 11, 5, True),
+              (1, 2, 2, 12, 6, 3, False)]
+    for (B, H, Hkv, Nq, Nk, d, causal) in shapes:
+        if causal and Nq > Nk:
+            continue
+        q = rng.standard_normal((B, Nq, H, d))
+        k = rng.standard_normal((B, Nk, Hkv, d))
+        v = rng.standard_normal((B, Nk, Hkv, d))
+        do = rng.standard_normal((B, Nq, H, d))
+        got = orc.attention_bwd(q, k, v, do, 0.43, causal)
+        want = _torch_grads(q, k, v, do, 0.43, causal)
+        for name, g, w in zip(("dQ", "dK", "dV"), got, want):
+            _close(g, w, tol=1e-12, what=f"{name} {B, H, Hkv, Nq, Nk, d, causal}")
+
+
+def pin_bwd_finite_differences(orc):
+    """Central differences of L = sum(dO * O) through the forward oracle (no backward code)."""
+    rng = np.random.default_rng(31)
+    B, H, Hkv, Nq, Nk, d = 1, 2, 1, 4, 6, 3
+    q = rng.standard_normal((B, Nq, H, d))
+    k = rng.standard_normal((B, Nk, Hkv, d))
+    v = rng.standard_normal((B, Nk, Hkv, d))
+    do = rng.standard_normal((B, Nq, H, d))
+    eps = 1e-5
+    for causal in (False, True):
+        grads = orc.attention_bwd(q, k, v, do, 0.8, causal)
+        for which, x in enumerate((q, k, v)):
+            for _ in range(6):
+                idx = tuple(int(rng.integers(n)) for n in x.shape)
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                lp = float(np.sum(do * orc.attention(*args_p, 0.8, causal)[0]))
+                lm = float(np.sum(do * orc.attention(*args_m, 0.8, causal)[0]))
+                fd = (lp - lm) / (2 * eps)
+                g = grads[which][idx]
+                assert abs(fd - g) <= 1e-7 * max(1.0, abs(g)), f"grad {which} {idx}: fd {fd} vs {g}"
+
+
+def pin_bwd_invariants(orc):
+    """Closed forms: per (batch, K/V head) the key gradients sum to zero (every row of dS
+    sums to zero); the value gradients sum to the upstream rows that see a key; equal keys
+    give dQ = 0; scale 0 gives dQ = dK = 0 and dV_j = sum of dO_i / (keys of row i)."""
+    rng = np.random.default_rng(32)
+    B, H, Hkv, Nq, Nk, d = 2, 4, 2, 6, 5, 3
+    q = rng.standard_normal((B, Nq, H, d))
+    k = rng.standard_normal((B, Nk, Hkv, d))
+    v = rng.standard_normal((B, Nk, Hkv, d))
+    do = rng.standard_normal((B, Nq, H, d))
+    G = H // Hkv
+    for causal in (False, True):
+        dq, dk, dv = orc.attention_bwd(q, k, v, do, 0.6, causal)
+        _close(dk.sum(axis=1), np.zeros((B, Hkv, d)), tol=1e-12, what="sum dK")
+        has_key = np.array([min(Nk, i + Nk - Nq + 1) > 0 if causal else True for i in range(Nq)])
+        want = (do * has_key[None, :, None, None]).sum(axis=1).reshape(B, Hkv, G, d).sum(axis=2)
+        _close(dv.sum(axis=1), want, tol=1e-12, what="sum dV")
+        ke = np.broadcast_to(k[:, :1], k.shape).copy()
+        dq_e, _, _ = orc.attention_bwd(q, ke, v, do, 0.6, causal)
+        _close(dq_e, np.zeros_like(dq_e), tol=1e-12, what="equal keys dQ")
+        dq0, dk0, dv0 = orc.attention_bwd(q, k, v, do, 0.0, causal)
+        _close(dq0, np.zeros_like(dq0), what="scale 0 dQ")
+        _close(dk0, np.zeros_like(dk0), what="scale 0 dK")
+        nk = np.array([max(0, min(Nk, i + Nk - Nq + 1)) if causal else Nk for i in range(Nq)])
+        want = np.zeros_like(dv0)
+        for i in range(Nq):
+            if nk[i]:
+                contrib = do[:, i].reshape(B, Hkv, G, d).sum(axis=2) / nk[i]
+                want[:, :nk[i]] += contrib[:, None]
+        _close(dv0, want, tol=1e-12, what="scale 0 dV")
+
+
+def pin_bwd_varlen_is_per_sequence(orc):
+    """Packed varlen gradients equal separate calls on each sequence."""
+    rng = np.random.default_rng(33)
+    lengths = [3, 1, 6]
+    H, Hkv, d = 4, 2, 3
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    T = off[-1]
+    q = rng.standard_normal((T, H, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    do = rng.standard_normal((T, H, d))
+    for causal in (False, True):
+        got = orc.attention_bwd_varlen(q, k, v, do, off, 0.5, causal)
+        for b in range(len(lengths)):
+            sl = slice(off[b], off[b + 1])
+            one = orc.attention_bwd(q[None, sl], k[None, sl], v[None, sl], do[None, sl], 0.5, causal)
+            for name, g, w in zip(("dQ", "dK", "dV"), got, one):
+                _close(g[sl], w[0], what=f"{name} seq {b}")
+
+
 ALL_PINS = [pin_worked_example, pin_causal_figure12, pin_bottom_right_alignment,
             pin_exercise7_bounds, pin_torch_sdpa, pin_rows_sum_to_one, pin_shift_invariance,
             pin_causal_row0, pin_convex_hull, pin_future_independence, pin_scale_zero_mean,
             pin_rows_without_keys, pin_key_permutation, pin_head_batch_slices,
             pin_varlen_is_per_sequence, pin_rows_match_full, pin_torch_sdpa_grouped_heads,
-            pin_gqa_exercise8, pin_gqa_equals_repeated_heads]
+            pin_gqa_exercise8, pin_gqa_equals_repeated_heads, pin_bwd_torch_autograd,
+            pin_bwd_finite_differences, pin_bwd_invariants, pin_bwd_varlen_is_per_sequence]

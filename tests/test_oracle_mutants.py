@@ -1,7 +1,8 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU) and check that
 the pins catch every one of them.  This shows the pins constrain each part of
 the oracle: the scale, the maximum subtraction, the normaliser, the key/value
-strides, the K/V head of each query head, the mask alignment and the LSE."""
+strides, the K/V head of each query head, the mask alignment, the LSE and the
+backward's terms."""
 import os
 import subprocess
 
@@ -30,6 +31,12 @@ MUTANTS = {
                        "                const double *vb = v + (b * Nk * Hkv + h % Hkv) * d;"),
     "kv_stride_query_heads": ("const int64_t stride = Hkv * d;     /* between consecutive keys */",
                               "const int64_t stride = H * d;     /* between consecutive keys */"),
+    "bwd_dq_without_scale": ("dqi[c] += scale * ds * k[j * kstride + c];", "dqi[c] += ds * k[j * kstride + c];"),
+    "bwd_no_row_term": ("const double ds = p_buf[j] * (dp_buf[j] - D);", "const double ds = p_buf[j] * dp_buf[j];"),
+    "bwd_dv_from_ds": ("dv[j * kstride + c] += p_buf[j] * doi[c];", "dv[j * kstride + c] += ds * doi[c];"),
+    "bwd_dk_from_dq_side": ("dk[j * kstride + c] += scale * ds * qi[c];", "dk[j * kstride + c] += scale * ds * doi[c];"),
+    "bwd_kv_head_modulo": ("for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)\n                    bwd_head(q + (b * Nq * H + h) * d",
+                           "for (int64_t h = kvh; h < H; h += Hkv)\n                    bwd_head(q + (b * Nq * H + h) * d"),
     "lse_wrong_slot": ("lse + (b * H + h) * Nq + i);", "lse + (h * B + b) * Nq + i);"),
 }
 
