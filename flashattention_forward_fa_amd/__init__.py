@@ -71,6 +71,13 @@ def load():
     lib.fa_fwd_opts_default.restype = None
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i
+    bwd = [vp] * 10 + [i, i, i, i, i, f, i, vp, i]
+    lib.fa_bwd.argtypes = bwd + [vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_check.argtypes = bwd
+    lib.fa_bwd_check.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -116,6 +123,24 @@ def fa_fwd_check(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets
     return load().fa_fwd_check(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk,
                                d, float(scale), int(causal), _ptr(varlen_offsets),
                                ctypes.byref(opts) if opts is not None else None)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale, causal,
+           varlen_offsets=None, kv_heads=0, stream=None) -> int:
+    return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                         _ptr(dk), _ptr(dv), _ptr(workspace), B, H, Nq, Nk, d, float(scale),
+                         int(causal), _ptr(varlen_offsets), int(kv_heads), _stream(stream))
+
+
+def fa_bwd_check(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale, causal,
+                 varlen_offsets=None, kv_heads=0) -> int:
+    return load().fa_bwd_check(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), B, H, Nq, Nk, d,
+                               float(scale), int(causal), _ptr(varlen_offsets), int(kv_heads))
+
+
+def fa_bwd_workspace_size(B: int, H: int, Nq: int) -> int:
+    return int(load().fa_bwd_workspace_size(B, H, Nq))
 
 
 def fa_status_string(status: int) -> str:
@@ -171,3 +196,36 @@ def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_s
     if st != FA_OK:
         raise FaError(st, "fa_fwd_ex")
     return o, lse
+
+
+def attention_bwd(q, k, v, o, lse, dout, scale: float, causal: bool, *, varlen_offsets=None,
+                  max_seqlen=None, stream=None):
+    """Allocate dQ, dK, dV and the workspace with torch and run fa_bwd.
+
+    Shapes and layouts as for attention(); o and lse are the forward's outputs
+    (o bf16) and dout is dO, shaped like o.  Returns (dq, dk, dv), bf16."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous bfloat16 tensor")
+    if varlen_offsets is None:
+        B, Nq, H, d = q.shape
+        Nk, Hkv = k.shape[1], k.shape[2]
+    else:
+        T, H, d = q.shape
+        Hkv = k.shape[1]
+        B = varlen_offsets.numel() - 1
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with varlen offsets")
+        Nq = Nk = int(max_seqlen)
+    if o.shape != q.shape or dout.shape != q.shape or v.shape != k.shape or H % Hkv:
+        raise ValueError("o and dout must be shaped like q, v like k, and Hkv must divide H")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws = torch.empty((fa_bwd_workspace_size(B, H, Nq) // 4,), dtype=torch.float32, device=q.device)
+    st = fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Nq, Nk, d, scale, causal,
+                varlen_offsets, Hkv, stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,7 +1,7 @@
 """Build libfa.so in-tree with hipcc for gfx950.
 
 The library is one shared object holding the C ABI (``csrc/fa_api.cpp``) and
-the HIP kernels (``csrc/fa_fwd_kernel.hip``).  Packed-fp32 VALU instructions
+the HIP kernels (``csrc/fa_fwd_kernel.hip``, ``csrc/fa_bwd_kernel.hip``).  Packed-fp32 VALU instructions
 are disabled for device code.
 """
 from __future__ import annotations
@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-SOURCES = [os.path.join(CSRC, "fa_fwd_kernel.hip"), os.path.join(CSRC, "fa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fa_fwd_kernel.hip"), os.path.join(CSRC, "fa_bwd_kernel.hip"),
+           os.path.join(CSRC, "fa_api.cpp")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

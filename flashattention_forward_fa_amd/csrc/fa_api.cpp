@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;   // 0.2.0: grouped K/V heads
+constexpr int kVersion = 300;   // 0.3.0: backward pass
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -48,9 +48,74 @@ int check_args(const void *q, const void *k, const void *v, const void *o, const
     return FA_OK;
 }
 
+int check_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+              const void *dout, const void *dq, const void *dk, const void *dv, const void *ws,
+              int B, int H, int Nq, int Nk, int d, float scale, int causal,
+              const int32_t *offsets, int kv_heads) {
+    fa_fwd_opts opts;
+    opts.o_dtype = FA_DTYPE_BF16;
+    opts.rescale_threshold = 8.0f;
+    opts.schedule = FA_SCHEDULE_AUTO;
+    opts.kv_heads = kv_heads;
+    const int st = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, offsets, opts);
+    if (st != FA_OK) return st;
+    if (!dout || !dq || !dk || !dv || !ws) return FA_ERR_INVALID_ARG;
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        ((uintptr_t)ws & 3u))
+        return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t fa_bwd_workspace_size(int B, int H, int Nq) {
+    if (B < 1 || H < 1 || Nq < 1) return 0;
+    return (int64_t)4 * B * H * Nq;
+}
+
+int fa_bwd_check(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, const void *dq, const void *dk, const void *dv,
+                 const void *workspace, int B, int H, int Nq, int Nk, int d, float scale,
+                 int causal, const int32_t *varlen_offsets, int kv_heads) {
+    return check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale, causal,
+                     varlen_offsets, kv_heads);
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, void *workspace,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           const int32_t *varlen_offsets, int kv_heads, void *stream) {
+    const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale,
+                             causal, varlen_offsets, kv_heads);
+    if (st != FA_OK) return st;
+    fa::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dsum = (float *)workspace;
+    p.offsets = varlen_offsets;
+    p.B = B;
+    p.H = H;
+    p.group = kv_heads > 0 ? H / kv_heads : 1;
+    p.Hkv = H / p.group;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.scale = scale;
+    // P = exp2(S * scale * log2 e - LSE * log2 e); scale_log2 computed in
+    // double and rounded once, with its sign (LSE is given, no maximum kept).
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
+    (void)hipGetLastError();
+    const int err = fa::launch_bwd(p, d, causal != 0, stream);
+    return err == 0 ? FA_OK : FA_ERR_HIP;
+}
 
 void fa_fwd_opts_default(fa_fwd_opts *opts) {
     if (!opts) return;

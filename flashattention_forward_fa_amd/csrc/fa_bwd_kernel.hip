@@ -1,0 +1,558 @@
+// fa_bwd_kernel.hip -- FlashAttention backward for gfx950 (MI355X).
+//
+// What is computed ("FlashAttention-4（下）", argus-lessons, section 1: the
+// backward recomputes S and P and forms the products dP, dV, dQ and dK):
+// for one (batch, head), with the forward's LSE and the upstream gradient dO,
+//
+//   P_ij  = exp(scale * q_i.k_j - LSE_i)          (recomputed, masked -> 0)
+//   D_i   = dO_i . O_i                            (pre-pass, one value per row)
+//   dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i)
+//   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
+//
+// The exponent is base 2 with the scale folded in: P = exp2(S * c - LSE * log2 e),
+// c = scale * log2 e (any sign: no running maximum is needed, LSE is given).
+//
+// Mapping onto CDNA4 (not the pages' Blackwell design -- no TMEM, 2-CTA MMA
+// or DSMEM here):
+// * Deterministic, no atomics: dQ is reduced over keys and dK, dV over queries
+//   by two kernels.  The key-block kernel (dK, dV) owns 128 keys per workgroup
+//   (32 per wave) and walks the query blocks; the query-block kernel (dQ) owns
+//   128 queries and walks the key blocks.  Each recomputes S and dP, so the
+//   pair issues 7 products per block pair instead of 5 -- the price of a fixed
+//   summation order without a global atomic or a lock.
+// * The query-block kernel is the forward's layout: S^T = K Q^T and
+//   dP^T = V dO^T with one query per lane (Q and dO fragments in registers),
+//   dS^T in bf16 as the B operand of dQ^T += K^T dS^T, K^T by transpose reads.
+// * The key-block kernel is its transpose: S = Q K^T and dP = dO V^T with one
+//   key per lane (K and V fragments in registers); P and dS in bf16 are the B
+//   operands of dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T by transpose
+//   reads.  The per-query LSE and D come from LDS, four rows per 16-byte read.
+// * Tiles in LDS use the swizzled layout of fa_device.h, free of bank
+//   conflicts for both the 16-byte row reads and the transpose reads.  Blocks
+//   are double-buffered through registers with one barrier per block.
+// * Grouped K/V heads: the key-block kernel of K/V head kv walks the query
+//   heads kv*G .. kv*G+G-1 in turn and writes dK, dV once.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+
+// ------------------------------------------------------------------ pre-pass
+// D_i = sum_c dO_ic O_ic in fp32 for every row (b, h, i); layout of LSE.
+// Each row is handled by D/8 lanes (16 bytes each), reduced by lane exchange.
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_dsum_kernel(BwdParams p) {
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int RPB = 256 / CPR;             // rows per workgroup
+    const int tid = threadIdx.x;
+    const int64_t row = (int64_t)blockIdx.x * RPB + tid / CPR;   // token-major: (token, head)
+    const int c = tid % CPR;
+    const int64_t T = p.offsets ? (int64_t)p.offsets[p.B] : (int64_t)p.B * p.Nq;
+    float acc = 0.f;
+    const bool ok = row < T * p.H;
+    if (ok) {
+        const u32x4 a = *(const u32x4 *)((const unsigned short *)p.dout + row * D + 8 * c);
+        const u32x4 b = *(const u32x4 *)((const unsigned short *)p.o + row * D + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
+            acc = fmaf(__uint_as_float(a[e] & 0xFFFF0000u), __uint_as_float(b[e] & 0xFFFF0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    if (ok && c == 0) {
+        const int64_t t = row / p.H;
+        const int h = (int)(row % p.H);
+        int64_t idx;
+        if (p.offsets) idx = (int64_t)h * T + t;
+        else           idx = ((t / p.Nq) * p.H + h) * (int64_t)p.Nq + t % p.Nq;
+        p.dsum[idx] = acc;
+    }
+}
+
+// ------------------------------------------------------------------ tile maps
+struct BwdTile {
+    int b, h;            // batch (sequence) and head (query head, or K/V head)
+    int m;               // tile index along the sequence
+    int tok0;            // first token of the sequence
+    int L_q, L_k;        // query and key lengths of the sequence
+};
+
+// Tiles of 128 rows along a sequence: (b, h, m) from the workgroup index t,
+// linear order.  heads = the head count of the owning dimension.
+__device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads, int len_max,
+                                           BwdTile &c) {
+    const int nm = (len_max + 127) / 128;
+    c.m = t % nm;
+    const int bh = t / nm;
+    c.b = bh / heads;
+    c.h = bh % heads;
+    if (p.offsets) {
+        c.tok0 = p.offsets[c.b];
+        c.L_q = c.L_k = p.offsets[c.b + 1] - c.tok0;
+        const int len = c.L_q;
+        return c.m * 128 < len;
+    }
+    c.tok0 = 0;
+    c.L_q = p.Nq;
+    c.L_k = p.Nk;
+    return true;
+}
+
+// ------------------------------------------------------------------ dQ kernel
+// Workgroup: 4 waves, 128 queries of one (b, h); K/V blocks of 64 keys.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
+    constexpr int BN = 64;
+    constexpr int NDS = D / 16, NDT = D / 32, NKT = BN / 32, NKS = BN / 16;
+    constexpr int TILE = BN * D;                       // elements of a K or V block
+    constexpr int CH = TILE / 8 / kBwdThreads;         // 16-byte chunks per thread per block
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE];
+    // K block in buffer b at smem + b * TILE, V block at smem + (2 + b) * TILE.
+
+    BwdTile tc;
+    if (!bwd_decode(blockIdx.x, p, p.H, p.Nq, tc)) return;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int Nq = tc.L_q, Nk = tc.L_k;
+    const int shift = Nk - Nq;
+    const int q0 = tc.m * 128 + 32 * w;                // first query of this wave
+    const int qrow = q0 + lq;
+    const bool row_ok = qrow < Nq;
+    const int hkv = tc.h / p.group;
+    const int64_t tq = (int64_t)p.H * D, tkv = (int64_t)p.Hkv * D;   // token strides
+    const unsigned tqb = (unsigned)(tq * 2), tkvb = (unsigned)(tkv * 2);
+    const int64_t qtok = (p.offsets ? tc.tok0 : (int64_t)tc.b * p.Nq);
+    const int64_t ktok = (p.offsets ? tc.tok0 : (int64_t)tc.b * p.Nk);
+    const unsigned short *Qg = (const unsigned short *)p.q + qtok * tq + tc.h * D;
+    const unsigned short *dOg = (const unsigned short *)p.dout + qtok * tq + tc.h * D;
+    const unsigned short *Kg = (const unsigned short *)p.k + ktok * tkv + hkv * D;
+    const unsigned short *Vg = (const unsigned short *)p.v + ktok * tkv + hkv * D;
+
+    // Keys this tile visits.
+    int nblocks = (Nk + BN - 1) / BN;
+    if (CAUSAL) {
+        const int last_row = min(tc.m * 128 + 128, Nq) - 1;
+        const int kmax = last_row + shift;
+        nblocks = kmax < 0 ? 0 : min(nblocks, kmax / BN + 1);
+    }
+
+    // Q and dO fragments (B operands, one query per lane) and the row terms.
+    bf16x8 qf[NDS], of[NDS];
+    {
+        const int rows = max(0, min(32, Nq - q0));
+        const unsigned bytes = rows > 0 ? (unsigned)(rows - 1) * tqb + (unsigned)(D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + (int64_t)q0 * tq, bytes);
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOg + (int64_t)q0 * tq, bytes);
+        const unsigned off = (unsigned)lq * tqb + (unsigned)(16 * g);
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            qf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off + 32u * ds));
+            of[ds] = __builtin_bit_cast(bf16x8, buffer_load16(ro, off + 32u * ds));
+        }
+    }
+    const float c = p.scale_log2;
+    float lse2 = 0.f, dsum = 0.f;
+    if (row_ok) {
+        int64_t idx;
+        if (p.offsets) idx = (int64_t)tc.h * p.offsets[p.B] + tc.tok0 + qrow;
+        else           idx = ((int64_t)tc.b * p.H + tc.h) * Nq + qrow;
+        lse2 = p.lse[idx] * 1.4426950408889634f;
+        dsum = p.dsum[idx];
+    }
+
+    f32x16 acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+
+    // Cooperative block loads: chunk u = tid + 256 * rr of a 64 x D block.
+    unsigned ld_off[CH];
+    int st_off[CH];
+#pragma unroll
+    for (int rr = 0; rr < CH; ++rr) {
+        const int u = tid + kBwdThreads * rr;
+        const int row = u / (D / 8), cc = u % (D / 8);
+        ld_off[rr] = (unsigned)row * tkvb + 16u * cc;
+        st_off[rr] = row * D + ((cc ^ vswz<D>(row)) << 3);
+    }
+    u32x4 kreg[CH], vreg[CH];
+    auto block_bytes = [&](int kb) -> unsigned {
+        const int rem = Nk - kb * BN;
+        if (kb >= nblocks || rem <= 0) return 0u;
+        return (unsigned)(min(rem, BN) - 1) * tkvb + (unsigned)(D * 2);
+    };
+    auto load = [&](int kb) {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)kb * BN * tkv, block_bytes(kb));
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)kb * BN * tkv, block_bytes(kb));
+#pragma unroll
+        for (int rr = 0; rr < CH; ++rr) {
+            kreg[rr] = buffer_load16(rk, ld_off[rr]);
+            vreg[rr] = buffer_load16(rv, ld_off[rr]);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int rr = 0; rr < CH; ++rr) {
+            *(u32x4 *)(smem + buf * TILE + st_off[rr]) = kreg[rr];
+            *(u32x4 *)(smem + (2 + buf) * TILE + st_off[rr]) = vreg[rr];
+        }
+    };
+
+    // Row-read offsets (A operand, 32 keys x 16 dims: key lq, chunk 2ds+g) and
+    // transpose-read offsets (K^T operand, as the forward's V^T).
+    int r_off[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) r_off[ds] = lq * D + (((2 * ds + g) ^ vswz<D>(lq)) << 3);
+    int t_off[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 4 * g + ((lane & 15) >> 2) + 8 * h;
+            const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            t_off[dt][h] = row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
+        }
+
+    if (nblocks > 0) {
+        load(0);
+        store(0);
+        __syncthreads();
+        for (int kb = 0; kb < nblocks; ++kb) {
+            const int buf = kb & 1;
+            if (kb + 1 < nblocks) load(kb + 1);
+            const unsigned short *Ks = smem + buf * TILE;
+            const unsigned short *Vs = smem + (2 + buf) * TILE;
+            // Uniform per wave: does any of its rows see a key of this block?
+            const bool live = q0 < Nq && (!CAUSAL || kb * BN <= min(q0 + 31, Nq - 1) + shift);
+            if (live) {
+                // S^T = K Q^T and dP^T = V dO^T for the 64 keys (32 per tile kt;
+                // 32-row tiles are 32 rows apart in the swizzled layout: the
+                // swizzle depends on the row within 16, unchanged by +32).
+                f32x16 s[NKT], dp[NKT];
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) { s[kt][i] = 0.f; dp[kt][i] = 0.f; }
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+                    for (int kt = 0; kt < NKT; ++kt) {
+                        const bf16x8 kf = *(const bf16x8 *)(Ks + r_off[ds] + 32 * kt * D);
+                        const bf16x8 vf = *(const bf16x8 *)(Vs + r_off[ds] + 32 * kt * D);
+                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt], 0, 0, 0);
+                        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[ds], dp[kt], 0, 0, 0);
+                    }
+                // dS^T = P^T (dP^T - D), masked keys -> 0; to bf16 B operands.
+                const int kv0 = kb * BN;
+                const int lim = row_ok ? (CAUSAL ? min(Nk - 1, qrow + shift) : Nk - 1) - kv0 - 4 * g
+                                       : -(1 << 30);
+                bf16x8 sf[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    unsigned wd[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float v2[2];
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const int i = 8 * (ks & 1) + 2 * e + h2;
+                            const int kt = ks >> 1;
+                            const int key = 32 * kt + 8 * (i >> 2) + (i & 3);   // relative to kv0 + 4g
+                            const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -lse2));
+                            v2[h2] = key > lim ? 0.f : pr * (dp[kt][i] - dsum);
+                        }
+                        wd[e] = pack_bf16x2(v2[0], v2[1]);
+                    }
+                    const u32x4 x = {wd[0], wd[1], wd[2], wd[3]};
+                    sf[ks] = __builtin_bit_cast(bf16x8, x);
+                }
+                // dQ^T += K^T dS^T.
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const unsigned short *a0 = Ks + 16 * ks * D;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + t_off[dt][0]));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + t_off[dt][1]));
+                        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
+                                                                          sf[ks], acc[dt], 0, 0, 0);
+                    }
+            }
+            if (kb + 1 < nblocks) store(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // dQ = scale * (dQ^T)^T, one query row per lane, bf16.
+    if (row_ok) {
+        unsigned short *Og = (unsigned short *)p.dq + (qtok + qrow) * tq + tc.h * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = 32 * dt + 8 * i4 + 4 * g;
+                const uint2 v2 = make_uint2(pack_bf16x2(acc[dt][4 * i4] * p.scale, acc[dt][4 * i4 + 1] * p.scale),
+                                            pack_bf16x2(acc[dt][4 * i4 + 2] * p.scale, acc[dt][4 * i4 + 3] * p.scale));
+                *(uint2 *)(Og + d0) = v2;
+            }
+    }
+}
+
+// ------------------------------------------------------------------ dK, dV kernel
+// Workgroup: 4 waves, 128 keys of one (b, K/V head); query blocks of 32.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
+    constexpr int BQ = 32;
+    constexpr int NDS = D / 16, NDT = D / 32, NQS = BQ / 16;
+    constexpr int TILE = BQ * D;                       // elements of a Q or dO block
+    constexpr int CH = TILE / 8 / kBwdThreads;         // 16-byte chunks per thread per block
+    static_assert(CH >= 1, "block must cover the threads");
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE];
+    __shared__ __attribute__((aligned(16))) float rowt[2][2][BQ];   // [buf][lse2, D][query]
+    // Q block in buffer b at smem + b * TILE, dO block at smem + (2 + b) * TILE.
+
+    BwdTile tc;
+    if (!bwd_decode(blockIdx.x, p, p.Hkv, p.Nk, tc)) return;   // tc.h is the K/V head
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
+    const int Nq = tc.L_q, Nk = tc.L_k;
+    const int shift = Nk - Nq;
+    const int k0w = tc.m * 128 + 32 * w;               // first key of this wave
+    const int key = k0w + lq;
+    const int64_t tq = (int64_t)p.H * D, tkv = (int64_t)p.Hkv * D;
+    const unsigned tqb = (unsigned)(tq * 2), tkvb = (unsigned)(tkv * 2);
+    const int64_t qtok = (p.offsets ? tc.tok0 : (int64_t)tc.b * p.Nq);
+    const int64_t ktok = (p.offsets ? tc.tok0 : (int64_t)tc.b * p.Nk);
+    const unsigned short *Kg = (const unsigned short *)p.k + ktok * tkv + tc.h * D;
+    const unsigned short *Vg = (const unsigned short *)p.v + ktok * tkv + tc.h * D;
+
+    // K and V fragments (B operands of S = Q K^T and dP = dO V^T, one key per lane).
+    bf16x8 kf[NDS], vf[NDS];
+    {
+        const int rows = max(0, min(32, Nk - k0w));
+        const unsigned bytes = rows > 0 ? (unsigned)(rows - 1) * tkvb + (unsigned)(D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)k0w * tkv, bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)k0w * tkv, bytes);
+        const unsigned off = (unsigned)lq * tkvb + (unsigned)(16 * g);
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            kf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off + 32u * ds));
+            vf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rv, off + 32u * ds));
+        }
+    }
+    const float c = p.scale_log2;
+
+    f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.f; dv[dt][i] = 0.f; }
+
+    // Query blocks this key tile meets: causal rows i with i + shift >= first key.
+    const int kfirst = tc.m * 128;
+    int qb0 = 0;
+    if (CAUSAL) qb0 = max(0, kfirst - shift) / BQ;
+    const int nqb = (Nq + BQ - 1) / BQ;
+    const bool wave_live = key - lq < Nk;   // the wave has at least one key
+
+    unsigned ld_off[CH];
+    int st_off[CH];
+#pragma unroll
+    for (int rr = 0; rr < CH; ++rr) {
+        const int u = tid + kBwdThreads * rr;
+        const int row = u / (D / 8), cc = u % (D / 8);
+        ld_off[rr] = (unsigned)row * tqb + 16u * cc;
+        st_off[rr] = row * D + ((cc ^ vswz<D>(row)) << 3);
+    }
+    u32x4 qreg[CH], oreg[CH];
+    float treg = 0.f;   // lse2 (threads 0..31) or D (threads 32..63) of one row
+    int cur_h = 0;
+    auto load = [&](int h, int qb) {
+        const unsigned short *Qg = (const unsigned short *)p.q + qtok * tq + h * D;
+        const unsigned short *Og = (const unsigned short *)p.dout + qtok * tq + h * D;
+        const int rem = Nq - qb * BQ;
+        const unsigned bytes = rem > 0 ? (unsigned)(min(rem, BQ) - 1) * tqb + (unsigned)(D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + (int64_t)qb * BQ * tq, bytes);
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(Og + (int64_t)qb * BQ * tq, bytes);
+#pragma unroll
+        for (int rr = 0; rr < CH; ++rr) {
+            qreg[rr] = buffer_load16(rq, ld_off[rr]);
+            oreg[rr] = buffer_load16(ro, ld_off[rr]);
+        }
+        if (tid < 2 * BQ) {
+            const int i = qb * BQ + (tid & (BQ - 1));
+            float v = 0.f;
+            if (i < Nq) {
+                int64_t idx;
+                if (p.offsets) idx = (int64_t)h * p.offsets[p.B] + tc.tok0 + i;
+                else           idx = ((int64_t)tc.b * p.H + h) * Nq + i;
+                v = tid < BQ ? p.lse[idx] * 1.4426950408889634f : p.dsum[idx];
+            }
+            treg = v;
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int rr = 0; rr < CH; ++rr) {
+            *(u32x4 *)(smem + buf * TILE + st_off[rr]) = qreg[rr];
+            *(u32x4 *)(smem + (2 + buf) * TILE + st_off[rr]) = oreg[rr];
+        }
+        if (tid < 2 * BQ) rowt[buf][tid / BQ][tid & (BQ - 1)] = treg;
+    };
+
+    int r_off[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) r_off[ds] = lq * D + (((2 * ds + g) ^ vswz<D>(lq)) << 3);
+    int t_off[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 4 * g + ((lane & 15) >> 2) + 8 * h;
+            const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            t_off[dt][h] = row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
+        }
+
+    const int steps_per_head = nqb - qb0;
+    const int nsteps = steps_per_head > 0 ? steps_per_head * p.group : 0;
+    if (nsteps > 0) {
+        cur_h = tc.h * p.group;
+        load(cur_h, qb0);
+        store(0);
+        __syncthreads();
+        for (int st = 0; st < nsteps; ++st) {
+            const int buf = st & 1;
+            const int h = tc.h * p.group + st / steps_per_head;
+            const int qb = qb0 + st % steps_per_head;
+            if (st + 1 < nsteps)
+                load(tc.h * p.group + (st + 1) / steps_per_head, qb0 + (st + 1) % steps_per_head);
+            (void)h;
+            const unsigned short *Qs = smem + buf * TILE;
+            const unsigned short *Os = smem + (2 + buf) * TILE;
+            const int qfirst = qb * BQ;
+            // Does this wave have a valid (query, key) pair in the block?
+            const bool live = wave_live && (!CAUSAL || qfirst + BQ - 1 + shift >= k0w);
+            if (live) {
+                f32x16 s, dp;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) {
+                    const bf16x8 qa = *(const bf16x8 *)(Qs + r_off[ds]);
+                    const bf16x8 oa = *(const bf16x8 *)(Os + r_off[ds]);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ds], dp, 0, 0, 0);
+                }
+                // Accumulator: lane = key, register i = query 8(i/4) + 4g + i%4.
+                // P and dS, masked pairs -> 0, to bf16 B operands (16 queries each).
+                const float4 *lrow = (const float4 *)rowt[buf][0];
+                const float4 *drow = (const float4 *)rowt[buf][1];
+                bf16x8 pfr[NQS], sfr[NQS];
+#pragma unroll
+                for (int qs = 0; qs < NQS; ++qs) {
+                    unsigned pw[4], sw[4];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int i0 = 8 * qs + 4 * hh;         // registers i0..i0+3
+                        const float4 l4 = lrow[(8 * (i0 >> 2) + 4 * g) >> 2];
+                        const float4 d4 = drow[(8 * (i0 >> 2) + 4 * g) >> 2];
+                        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+                        float pv[4], sv[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int qi = qfirst + 8 * ((i0 + e) >> 2) + 4 * g + e;
+                            const bool ok = key < Nk && qi < Nq && (!CAUSAL || key <= qi + shift);
+                            const float pr = __builtin_amdgcn_exp2f(fmaf(s[i0 + e], c, -lv[e]));
+                            pv[e] = ok ? pr : 0.f;
+                            sv[e] = pv[e] * (dp[i0 + e] - dvv[e]);
+                        }
+                        pw[2 * hh] = pack_bf16x2(pv[0], pv[1]);
+                        pw[2 * hh + 1] = pack_bf16x2(pv[2], pv[3]);
+                        sw[2 * hh] = pack_bf16x2(sv[0], sv[1]);
+                        sw[2 * hh + 1] = pack_bf16x2(sv[2], sv[3]);
+                    }
+                    const u32x4 xp = {pw[0], pw[1], pw[2], pw[3]};
+                    const u32x4 xs = {sw[0], sw[1], sw[2], sw[3]};
+                    pfr[qs] = __builtin_bit_cast(bf16x8, xp);
+                    sfr[qs] = __builtin_bit_cast(bf16x8, xs);
+                }
+                // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transpose reads).
+#pragma unroll
+                for (int qs = 0; qs < NQS; ++qs)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const unsigned short *o0 = Os + 16 * qs * D;
+                        const unsigned short *q0p = Qs + 16 * qs * D;
+                        const i16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(o0 + t_off[dt][0]));
+                        const i16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(o0 + t_off[dt][1]));
+                        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(q0p + t_off[dt][0]));
+                        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(q0p + t_off[dt][1]));
+                        const i16x8 ob = __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const i16x8 qbv = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ob),
+                                                                         pfr[qs], dv[dt], 0, 0, 0);
+                        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qbv),
+                                                                         sfr[qs], dk[dt], 0, 0, 0);
+                    }
+            }
+            if (st + 1 < nsteps) store(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // dK = scale * (dK^T)^T and dV, one key row per lane, bf16.
+    if (key < Nk) {
+        unsigned short *dKg = (unsigned short *)p.dk + (ktok + key) * tkv + tc.h * D;
+        unsigned short *dVg = (unsigned short *)p.dv + (ktok + key) * tkv + tc.h * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = 32 * dt + 8 * i4 + 4 * g;
+                const float sc = p.scale;
+                *(uint2 *)(dKg + d0) = make_uint2(pack_bf16x2(dk[dt][4 * i4] * sc, dk[dt][4 * i4 + 1] * sc),
+                                                  pack_bf16x2(dk[dt][4 * i4 + 2] * sc, dk[dt][4 * i4 + 3] * sc));
+                *(uint2 *)(dVg + d0) = make_uint2(pack_bf16x2(dv[dt][4 * i4], dv[dt][4 * i4 + 1]),
+                                                  pack_bf16x2(dv[dt][4 * i4 + 2], dv[dt][4 * i4 + 3]));
+            }
+    }
+}
+
+template <int D>
+static int launch_bwd_d(const BwdParams &p, bool causal, hipStream_t s) {
+    const int64_t rows = (int64_t)p.B * p.Nq * p.H;          // upper bound for varlen
+    const int rpb = 256 / (D / 8);
+    hipLaunchKernelGGL((fa_bwd_dsum_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, p);
+    const unsigned gq = (unsigned)((int64_t)p.B * p.H * ((p.Nq + 127) / 128));
+    const unsigned gk = (unsigned)((int64_t)p.B * p.Hkv * ((p.Nk + 127) / 128));
+    if (causal) {
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, true>), dim3(gq), dim3(kBwdThreads), 0, s, p);
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, true>), dim3(gk), dim3(kBwdThreads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, false>), dim3(gq), dim3(kBwdThreads), 0, s, p);
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, false>), dim3(gk), dim3(kBwdThreads), 0, s, p);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_bwd(const BwdParams &p, int d, bool causal, void *stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (d == 64) return launch_bwd_d<64>(p, causal, s);
+    return launch_bwd_d<128>(p, causal, s);
+}
+
+}  // namespace fa

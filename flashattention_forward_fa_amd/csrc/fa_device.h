@@ -1,0 +1,72 @@
+// fa_device.h -- device helpers shared by the forward and backward kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+
+// Swizzled tile layout in LDS (rows of D bf16 values, e.g. keys of a V block):
+// row r holds its 16-byte chunks with chunk c stored at position c ^ vswz<D>(r).
+// Two read patterns must be free of bank conflicts:
+//  * transpose reads (ds_read_b64_tr_b16), served 32 lanes at a time: lanes
+//    0-31 read rows 4g+0..3 (+8, +16 k) at the four chunks 4t..4t+3;
+//  * 16-byte row reads, served 16 lanes at a time: rows 0..15 at one chunk.
+// At D = 128 a row is 256 B (all 64 banks), so f must be a permutation of
+// 0..15 over 16 consecutive rows and give rows 4g+0..3 disjoint quarters.  At
+// D = 64 a row is 128 B: odd rows sit on the upper 32 banks, rows r and r+2
+// must take opposite 64-byte halves, and the 8 even (odd) rows of a 16-row
+// read must land on distinct chunks.  16-byte writes are conflict-free in any
+// layout.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) ^ ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ float lane_pair_max(float x) {
+    // Combine lanes l and l^32 (both halves see the maximum of the pair).
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float lane_pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+    const f32x2 f = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+// Sum of the two bf16 halves of a word, accumulated in fp32 (v_dot2 with (1, 1)).
+__device__ __forceinline__ float add_bf16x2(unsigned word, float acc) {
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc, false);
+}
+
+// Global loads go through buffer resources: a descriptor per K/V block whose
+// range ends at the block's last valid key, so keys past the end read as 0
+// with no branch and no address arithmetic per block.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+}  // namespace fa

@@ -61,18 +61,10 @@
 
 #include <type_traits>
 
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D_>
 struct Tile {
@@ -94,42 +86,6 @@ struct Tile {
     static_assert(KCH % NT == 0, "K block must split evenly over the threads");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
-
-// V tile layout in LDS: row r (a key) holds its D values as 16-byte chunks,
-// chunk c stored at position c ^ vswz<D>(r).  A transpose read serves 32
-// lanes at once: lanes 0-31 read rows 4g+0..3 (+8, +16 ks) at four chunks
-// 4dt..4dt+3, and the swizzle puts those four rows on disjoint banks
-// (rows of 256 B at D = 128 start on bank 0, so each row gets its own
-// quarter; rows of 128 B at D = 64 pair up on a bank base, so rows r and
-// r + 2 take opposite halves).  16-byte writes are conflict-free either way.
-template <int D>
-__device__ __forceinline__ int vswz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) ^ ((r >> 2) & 3);
-    else return ((r >> 1) & 1) << 2;
-}
-
-__device__ __forceinline__ float lane_pair_max(float x) {
-    // Combine lanes l and l^32 (both halves see the maximum of the pair).
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float lane_pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-    const f32x2 f = {a, b};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
-}
-
-// Sum of the two bf16 halves of a word, accumulated in fp32 (v_dot2 with (1, 1)).
-__device__ __forceinline__ float add_bf16x2(unsigned word, float acc) {
-    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc, false);
-}
 
 // ------------------------------------------------------------------ scheduler
 // Map the workgroup index to (batch, head, query tile).  Returns false when
@@ -226,18 +182,6 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
 }
 
 // ------------------------------------------------------------------ kernel
-// Global loads go through buffer resources: a descriptor per K/V block whose
-// range ends at the block's last valid key, so keys past the end read as 0
-// with no branch and no address arithmetic per block.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
-}
-
 template <int D, bool CAUSAL, bool VARLEN, typename OutT>
 __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     using T = Tile<D>;

@@ -38,4 +38,18 @@ struct FwdParams {
 // Enqueue the forward kernel; returns a hipError_t value (0 = success).
 int launch_fwd(const FwdParams &p, int d, bool causal, OutType out, void *stream);
 
+struct BwdParams {
+    const void *q, *k, *v, *o, *dout;   // bf16 inputs (o: the forward's output)
+    const float *lse;                   // the forward's LSE
+    void *dq, *dk, *dv;                 // bf16 gradients
+    float *dsum;                        // workspace: D_i = dO_i . O_i, layout of LSE
+    const int32_t *offsets;             // varlen: int32 [B+1]; nullptr for fixed length
+    int B, H, Hkv, group, Nq, Nk;       // varlen: Nq = Nk = upper bound of the lengths
+    float scale;                        // s (any finite value)
+    float scale_log2;                   // s * log2(e)
+};
+
+// Enqueue the backward kernels (row sums D, then dQ, then dK and dV).
+int launch_bwd(const BwdParams &p, int d, bool causal, void *stream);
+
 }  // namespace fa

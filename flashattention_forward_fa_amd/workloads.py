@@ -18,6 +18,8 @@ Recipe (every draw is seeded, ``numpy.random.default_rng`` / PCG64):
   int32 cumulative offsets [0, L0, L0+L1, ...] describe the packing.
 * Grouped K/V heads: K and V are drawn with Hkv heads ([.., Hkv, dim]); with
   Hkv = H the draws are the multi-head ones.
+* The backward's upstream gradient dO: standard_normal shaped like O, from its
+  own seed, rounded to bf16.
 
 The named workloads mirror the five synthetic configurations the method is
 measured on (seed = 1000 + number).
@@ -172,6 +174,14 @@ def make_varlen(H, d, *, seed, causal=True, lengths=None, nseq=16, len_lo=128, l
                     d, bool(causal), float(scale), o_dtype, seed,
                     bf16_bits(q), bf16_bits(k), bf16_bits(v),
                     offsets=offsets.astype(np.int32), lengths=lengths, Hkv=Hkv)
+
+
+def make_dout(w: Workload, seed: int) -> np.ndarray:
+    """Upstream gradient dO for workload w (the backward's input): bf16 bits of
+    float32 standard_normal draws shaped like O ([B,Nq,H,d] or [T,H,d])."""
+    rng = np.random.default_rng(seed)
+    shape = (w.total_tokens, w.H, w.d) if w.varlen else (w.B, w.Nq, w.H, w.d)
+    return bf16_bits(rng.standard_normal(shape, dtype=np.float32))
 
 
 CONFIG_NAMES = {

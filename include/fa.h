@@ -128,6 +128,42 @@ int fa_fwd_check(const void *q, const void *k, const void *v, const void *o,
                  const float *lse, int B, int H, int Nq, int Nk, int d, float scale,
                  int causal, const int32_t *varlen_offsets, const fa_fwd_opts *opts);
 
+/*
+ * Backward pass: the gradients dQ, dK, dV of the forward's O for an upstream
+ * gradient dO ("FlashAttention-4（下）", argus-lessons, section 1: recompute S
+ * and P, then dP = dO V^T, dV = P^T dO, dS = P (dP - rowsum(dO O)),
+ * dQ = scale dS K, dK = scale dS^T Q).
+ *
+ *   q, k, v      : the forward's inputs (bf16), layouts as for fa_fwd_ex
+ *   o, lse       : the forward's outputs for these inputs (o bf16, lse fp32)
+ *   dout         : dO, bf16, laid out like o
+ *   dq           : bf16, like q; dk, dv: bf16, like k and v
+ *   workspace    : device memory of fa_bwd_workspace_size(B, H, Nq) bytes,
+ *                  owned by the caller, 4-byte aligned; its contents are
+ *                  scratch (no state is kept across calls)
+ *   kv_heads     : K/V heads Hkv (0 = H), as opts.kv_heads of fa_fwd_ex;
+ *                  dk and dv sum over the query heads of each K/V head
+ *   scale, causal, varlen_offsets, B, H, Nq, Nk, d, stream: as for fa_fwd_ex
+ *
+ * The result is deterministic: no atomics; dQ and dK/dV are reduced by two
+ * kernels in a fixed order.  Checks and errors as for fa_fwd_ex (plus null
+ * or misaligned o, dout, dq, dk, dv, workspace).
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, void *workspace,
+           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+           const int32_t *varlen_offsets, int kv_heads, void *stream);
+
+/* Bytes of workspace fa_bwd needs (4 * B * H * Nq; for varlen B * Nq bounds
+ * the packed token count). */
+int64_t fa_bwd_workspace_size(int B, int H, int Nq);
+
+/* The argument checks of fa_bwd alone (no HIP call). */
+int fa_bwd_check(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                 const void *dout, const void *dq, const void *dk, const void *dv,
+                 const void *workspace, int B, int H, int Nq, int Nk, int d, float scale,
+                 int causal, const int32_t *varlen_offsets, int kv_heads);
+
 /* A static, NUL-terminated description of a status code. */
 const char *fa_status_string(int status);
 

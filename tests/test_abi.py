@@ -24,7 +24,8 @@ def test_exports_every_declared_function():
     lib = ctypes.CDLL(fa.library_path())
     names = declared_functions()
     assert {"fa_fwd", "fa_fwd_ex", "fa_fwd_check", "fa_status_string",
-            "fa_fwd_opts_default", "fa_version"} <= set(names)
+            "fa_fwd_opts_default", "fa_version", "fa_bwd", "fa_bwd_check",
+            "fa_bwd_workspace_size"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
 
@@ -121,3 +122,51 @@ def test_rejected_launch_makes_no_hip_call():
     assert st == fa.FA_ERR_INVALID_ARG
     st = fa.fa_fwd(P, P, P, P, P, 1, 1, 16, 16, 96, 0.1, 0, None, stream=0)
     assert st == fa.FA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ backward entry points
+
+def bcheck(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, ws=P, B=2, H=4, Nq=100, Nk=100,
+             d=128, scale=0.1, causal=1, varlen_offsets=None, kv_heads=0)
+    a.update(kw)
+    return fa.fa_bwd_check(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                           a["dv"], a["ws"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                           a["causal"], a["varlen_offsets"], a["kv_heads"])
+
+
+def test_bwd_valid_arguments():
+    assert bcheck() == fa.FA_OK
+    assert bcheck(d=64, causal=0, kv_heads=2) == fa.FA_OK
+    assert bcheck(varlen_offsets=P, Nq=512, Nk=512) == fa.FA_OK
+    assert bcheck(scale=-1.0) == fa.FA_OK and bcheck(scale=0.0) == fa.FA_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"])
+def test_bwd_null_pointer(field):
+    assert bcheck(**{field: None}) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field", ["dout", "dq", "dk", "dv"])
+def test_bwd_misaligned(field):
+    assert bcheck(**{field: P + 8}) == fa.FA_ERR_INVALID_ARG
+
+
+def test_bwd_rules():
+    assert bcheck(ws=P + 2) == fa.FA_ERR_INVALID_ARG          # workspace: 4-byte aligned
+    assert bcheck(ws=P + 4) == fa.FA_OK
+    assert bcheck(kv_heads=3) == fa.FA_ERR_INVALID_ARG         # must divide H
+    assert bcheck(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert bcheck(causal=2) == fa.FA_ERR_INVALID_ARG
+    assert bcheck(scale=math.nan) == fa.FA_ERR_INVALID_ARG
+    assert bcheck(varlen_offsets=P, Nq=100, Nk=200) == fa.FA_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_size():
+    assert fa.fa_bwd_workspace_size(2, 4, 100) == 4 * 2 * 4 * 100
+    assert fa.fa_bwd_workspace_size(0, 4, 100) == 0
+
+
+def test_bwd_rejected_launch_makes_no_hip_call():
+    st = fa.fa_bwd(P, P, P, P, P, None, P, P, P, P, 1, 1, 16, 16, 128, 0.1, 0, None, 0, stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG

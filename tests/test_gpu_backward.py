@@ -1,0 +1,138 @@
+"""Backward pass (fa_bwd) vs the fp64 oracle, through the C ABI.
+
+The GPU gets the forward's own outputs (O in bf16, LSE) and an upstream
+gradient dO; the oracle recomputes everything in fp64 from Q, K, V and dO.
+Bound, per gradient tensor G (dQ, dK, dV) with reference R, element-wise:
+
+    |G - R| <= 2^-7 |R| + 0.05 * rms(R) + 1e-5,   mean |G - R| <= 3e-3 * rms(R)
+
+Where the error comes from: the products that form the gradients take bf16
+operands (P and dS rounded, 2^-9 relative each, independent over the summed
+terms) and the result is rounded to bf16 (2^-9 relative) -- the 2^-7 |R| part.
+D_i = rowsum(dO_i * O_i) uses O as the forward returns it, in bf16, so
+D_i carries an error up to 2^-9 sum_c |dO_ic O_ic|; it shifts every dS_ij of
+the row by P_ij times that error and so dQ_i by s * dD_i * sum_j P_ij k_j.  On
+short causal rows (a handful of keys, P near 1) that term reaches a few
+percent of the typical gradient size, hence the rms part.  The 1e-5 floor is
+for gradients that are exactly zero (a row with one key has dS = 0; the GPU
+gets dP - D rounded, about 1e-7).  Measured over these tests: the mean error
+is 0.001-0.002 * rms(R), the bf16 rounding of the output; the largest errors,
+up to 0.2 * rms(R), sit on large elements, within 2^-7 of their value.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from flashattention_forward_fa_amd import workloads as wl
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import flashattention_forward_fa_amd as fa
+    fa.load()
+
+
+def run_bwd(w, dout_bits):
+    import torch
+    import flashattention_forward_fa_amd as fa
+    q, k, v, off = parity.to_device(w)
+    ms = w.Nq if w.varlen else None
+    o, lse = fa.attention(q, k, v, w.scale, w.causal, varlen_offsets=off, max_seqlen=ms)
+    do = torch.from_numpy(dout_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    dq, dk, dv = fa.attention_bwd(q, k, v, o, lse, do, w.scale, w.causal,
+                                  varlen_offsets=off, max_seqlen=ms)
+    torch.cuda.synchronize()
+    return tuple(t.double().cpu().numpy() for t in (dq, dk, dv))
+
+
+def ref_bwd(w, dout_bits):
+    q, k, v = parity.inputs_f64(w)
+    do = wl.bf16_to_f64(dout_bits)
+    if w.varlen:
+        return oracle.attention_bwd_varlen(q, k, v, do, w.offsets, w.scale, w.causal)
+    return oracle.attention_bwd(q, k, v, do, w.scale, w.causal)
+
+
+def compare_grads(got, ref, what):
+    stats = {}
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert g.shape == r.shape, f"{what} {name} shape"
+        assert np.all(np.isfinite(g)), f"{what} {name} not finite"
+        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+        err = np.abs(g - r)
+        bound = 2.0 ** -7 * np.abs(r) + 0.05 * rms + 1e-5
+        stats[name] = dict(max_err=float(err.max(initial=0.0)), rms=rms,
+                           max_over_rms=float(err.max(initial=0.0) / rms) if rms else 0.0,
+                           mean_over_rms=float(err.mean() / rms) if rms and err.size else 0.0)
+        bad = err > bound
+        if bad.any():
+            idx = np.unravel_index(np.argmax(err - bound), err.shape)
+            raise AssertionError(f"{what} {name}: error {err[idx]:.3e} > {bound[idx]:.3e} at {idx} "
+                                 f"(ref {r[idx]:.4f}, got {g[idx]:.4f}, rms {rms:.3e}); "
+                                 f"{int(bad.sum())} elements")
+        if rms:
+            assert err.mean() <= 3e-3 * rms, f"{what} {name}: mean error {err.mean():.3e} vs rms {rms:.3e}"
+    return stats
+
+
+SHAPES = [
+    # B, H, Hkv, Nq, Nk, d, causal
+    (1, 2, 2, 100, 100, 64, False),
+    (2, 3, 3, 300, 300, 64, True),
+    (1, 4, 4, 257, 257, 128, True),
+    (1, 2, 2, 64, 64, 128, False),
+    (1, 2, 2, 100, 300, 128, True),     # Nq < Nk
+    (1, 2, 2, 300, 100, 128, True),     # Nq > Nk: leading rows have no key
+    (2, 4, 2, 200, 200, 128, True),     # grouped K/V heads
+    (1, 4, 1, 129, 129, 64, False),     # one K/V head
+    (2, 1, 1, 1, 1, 64, True),
+    (1, 2, 2, 1, 500, 128, False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}H{}kv{}q{}k{}d{}{}".format(*s[:6], "c" if s[6] else "f"))
+def test_bwd_small(shape):
+    B, H, Hkv, Nq, Nk, d, causal = shape
+    w = wl.make_fixed(B, H, Nq, Nk, d, seed=7000 + Nq + Nk + d + H, causal=causal, Hkv=Hkv)
+    do = wl.make_dout(w, seed=8000 + Nq)
+    stats = compare_grads(run_bwd(w, do), ref_bwd(w, do), w.name)
+    print(w.name, stats)
+
+
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
+def test_bwd_scales(scale):
+    w = wl.make_fixed(1, 2, 150, 200, 64, seed=71, causal=True, scale=scale)
+    do = wl.make_dout(w, seed=72)
+    compare_grads(run_bwd(w, do), ref_bwd(w, do), f"scale {scale}")
+
+
+def test_bwd_varlen():
+    w = wl.make_varlen(4, 64, seed=73, lengths=[300, 1, 129, 513], causal=True, Hkv=2)
+    do = wl.make_dout(w, seed=74)
+    print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "varlen d64 causal"))
+    w = wl.make_varlen(2, 128, seed=75, lengths=[77, 256], causal=False)
+    do = wl.make_dout(w, seed=76)
+    print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "varlen d128 full"))
+
+
+def test_bwd_mid_size():
+    """Many key and query blocks: B=1, H=4, N=1024, d=128, causal."""
+    w = wl.make_fixed(1, 4, 1024, 1024, 128, seed=77, causal=True)
+    do = wl.make_dout(w, seed=78)
+    print(compare_grads(run_bwd(w, do), ref_bwd(w, do), w.name))
+
+
+def test_bwd_deterministic():
+    """Two calls give the same bits (no atomics, fixed reduction order)."""
+    w = wl.make_fixed(2, 4, 333, 333, 128, seed=79, causal=True, Hkv=2)
+    do = wl.make_dout(w, seed=80)
+    a = run_bwd(w, do)
+    b = run_bwd(w, do)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
