@@ -17,6 +17,12 @@ Prints one JSON line:
                kernel source as it is now)
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same
                workload (whole (batch, head) slices until ~10 s have passed)
+
+With --backward a step is one fa_bwd call (three launches: the row term
+D = rowsum(dO*O), the dQ kernel, the dK/dV kernel) on the forward's O and LSE
+and a seeded dO; its flops are counted as 2.5x the forward's (the five
+products of the gradient), the events bracket the whole call, and traffic is
+null.
 """
 from __future__ import annotations
 
@@ -62,12 +68,15 @@ def traffic_from_profile(workload: str):
         return None
 
 
-def cpu_baseline(w, budget_s: float):
-    """Time the oracle on whole (sequence, head) slices of the workload until budget_s."""
+def cpu_baseline(w, budget_s: float, backward: bool = False):
+    """Time the oracle on whole (sequence, head) slices of the workload until budget_s
+    (the backward: gradients of one slice's O for the seeded dO)."""
     import oracle
     from flashattention_forward_fa_amd import workloads as wl
     orc = oracle.default()
     d = w.d
+    group = w.H // w.kv_heads
+    dout_bits = wl.make_dout(w, seed=w.seed + 500) if backward else None
     if w.varlen:
         units = [(b, h) for h in range(w.H) for b in range(len(w.lengths))]
     else:
@@ -76,26 +85,37 @@ def cpu_baseline(w, budget_s: float):
     spent = 0.0
     done = 0
     for (b, h) in units:
+        hk = h // group
         if w.varlen:
             sl = slice(int(w.offsets[b]), int(w.offsets[b + 1]))
-            pick = lambda x: wl.bf16_to_f64(x[sl, h:h + 1])[None]
+            pick = lambda x, j: wl.bf16_to_f64(x[sl, j:j + 1])[None]
             Nq = Nk = int(w.lengths[b])
         else:
-            pick = lambda x: wl.bf16_to_f64(x[b:b + 1, :, h:h + 1])
+            pick = lambda x, j: wl.bf16_to_f64(x[b:b + 1, :, j:j + 1])
             Nq, Nk = w.Nq, w.Nk
-        q, k, v = pick(w.q), pick(w.k), pick(w.v)
-        t0 = time.perf_counter()
-        orc.attention(q, k, v, w.scale, w.causal)
+        q, k, v = pick(w.q, h), pick(w.k, hk), pick(w.v, hk)
+        if backward:
+            dout = pick(dout_bits, h)
+            t0 = time.perf_counter()
+            orc.attention_bwd(q, k, v, dout, w.scale, w.causal)
+        else:
+            t0 = time.perf_counter()
+            orc.attention(q, k, v, w.scale, w.causal)
         spent += time.perf_counter() - t0
-        per = 4.0 * Nq * Nk * d
+        per = 4.0 * Nq * Nk * d * (2.5 if backward else 1.0)
         flops += per / 2.0 if w.causal else per
         done += 1
         if spent >= budget_s:
             break
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+    what = "fp64 backward (forward recomputed, then dQ, dK, dV)" if backward else \
+        "fp64 three-pass"
+    # The backward's parallel loop runs over (batch, K/V head): one slice per call is
+    # one thread.  The forward's runs over query rows and uses every thread.
+    cores = 1 if backward else orc.num_threads()
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{done} of {len(units)} (sequence, head) slices, every query row of each, "
-                      f"fp64 three-pass, {spent:.1f} s"}
+                      f"{what}, {spent:.1f} s"}
 
 
 def main():
@@ -106,6 +126,8 @@ def main():
                     help="untimed steps first; the clocks take a few hundred launches to settle")
     ap.add_argument("--config", type=int, default=3, help="workload 1-5 (3 = the headline)")
     ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fa_bwd (dQ, dK, dV for the forward's outputs) instead of fa_fwd")
     ap.add_argument("--kv-heads", type=int, default=0,
                     help="grouped K/V heads for workloads 2-4 (0 = as many as query heads)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -121,6 +143,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     import flashattention_forward_fa_amd as fa
     from flashattention_forward_fa_amd import workloads as wl
@@ -164,6 +187,23 @@ def main():
         if st != fa.FA_OK:
             raise fa.FaError(st)
 
+    if args.backward:
+        # The backward's inputs: the forward's O (bf16) and LSE, a seeded dO.
+        if odt != fa.FA_DTYPE_BF16:
+            raise SystemExit("the backward takes a bf16 O: use a workload with bf16 output")
+        step()
+        dout = torch.from_numpy(wl.make_dout(w, seed=w.seed + 500).view(np.int16)).view(
+            torch.bfloat16).to("cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty((fa.fa_bwd_workspace_size(w.B, w.H, w.Nq) // 4,), dtype=torch.float32,
+                         device="cuda")
+
+        def step():  # noqa: F811 -- the timed step is the backward
+            st = fa.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, w.B, w.H, w.Nq, w.Nk, w.d,
+                           w.scale, int(w.causal), off, w.kv_heads, stream)
+            if st != fa.FA_OK:
+                raise fa.FaError(st)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -192,12 +232,16 @@ def main():
     sorted_ms = sorted(launch_ms)
     median_launch_ms = sorted_ms[len(sorted_ms) // 2]
 
-    flops = w.flops()
+    flops = w.flops() * (2.5 if args.backward else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = traffic_from_profile(w.name)
+    traffic = None if args.backward else traffic_from_profile(w.name)
+    metric = "attention fwd TFLOP/s and % of bf16 MFMA peak (d=128, N=4096 causal)"
+    if args.backward:
+        metric = ("attention bwd TFLOP/s (algorithmic flops 2.5x the forward's: five products) "
+                  "and % of bf16 MFMA peak")
     result = {
-        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak (d=128, N=4096 causal)",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -221,7 +265,7 @@ def main():
                      "algorithmic_hbm_bytes": w.io_bytes()},
     }
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.backward)
     print(json.dumps(result), flush=True)
 
 
