@@ -1,8 +1,8 @@
 """Build libfa.so in-tree with hipcc for gfx950.
 
 The library is one shared object holding the C ABI (``csrc/fa_api.cpp``) and
-the HIP kernels (``csrc/fa_fwd_kernel.hip``, ``csrc/fa_bwd_kernel.hip``).  Packed-fp32 VALU instructions
-are disabled for device code.
+the HIP kernels (``csrc/fa_fwd_kernel.hip``, ``csrc/fa_bwd_kernel.hip``).  Packed-fp32 VALU
+instructions are disabled for device code.
 """
 from __future__ import annotations
 
@@ -18,9 +18,14 @@ SOURCES = [os.path.join(CSRC, "fa_fwd_kernel.hip"), os.path.join(CSRC, "fa_bwd_k
            os.path.join(CSRC, "fa_api.cpp")]
 ARCH = "gfx950"
 
+# -amdgpu-mfma-vgpr-form: MFMA results and accumulators in ordinary VGPRs.  The
+# backward kernels hold more accumulators than the compiler's AGPR heuristic
+# expects and otherwise get register-file copies of them every block; the
+# forward kernel's code is the same either way.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
 ]
 

@@ -78,6 +78,45 @@ __global__ __launch_bounds__(256) void fa_bwd_dsum_kernel(BwdParams p) {
     }
 }
 
+// ------------------------------------------------------------------ LDS offsets
+// A lane's swizzled read offsets (elements) into a row-major D-wide tile, each
+// family kept as two registers instead of one per read.  With f = vswz(row):
+// * row reads (16-byte chunk 2*ds + g of row lq): the chunk index XOR f splits
+//   as 2*(ds ^ (f>>1)) + (g ^ (f&1)), so offset(ds) = base + ((16*ds) ^ x);
+// * transpose reads (rows 4g + (lane%16)/4 + 8h, columns 32*dt + 16*((lane/16)&1)
+//   + 4*(lane%4)): the chunk is 4*dt + s with s < 4, and (4*dt + s) ^ f splits as
+//   4*(dt ^ (f>>2)) + (s ^ (f&3)), so offset(dt, h) = base_h + ((32*dt) ^ x_h).
+struct LdsOffsets {
+    int rb, rx;          // row reads
+    int tb[2], tx[2];    // transpose reads, h = 0, 1
+    __device__ __forceinline__ int row(int ds) const { return rb + ((16 * ds) ^ rx); }
+    __device__ __forceinline__ int tr(int dt, int h) const { return tb[h] + ((32 * dt) ^ tx[h]); }
+    // Make the bases opaque for one loop iteration so that the per-read sums
+    // are formed next to their reads instead of being hoisted into one live
+    // register per read.
+    __device__ __forceinline__ void refresh() {
+        asm volatile("" : "+v"(rb), "+v"(rx), "+v"(tb[0]), "+v"(tx[0]), "+v"(tb[1]), "+v"(tx[1]));
+    }
+};
+
+template <int D>
+__device__ __forceinline__ LdsOffsets lds_offsets(int lane) {
+    const int lq = lane & 31, g = lane >> 5;
+    LdsOffsets o;
+    const int f = vswz<D>(lq);
+    o.rb = lq * D + 8 * (g ^ (f & 1));
+    o.rx = 16 * (f >> 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = 4 * g + ((lane & 15) >> 2) + 8 * h;
+        const int fr = vswz<D>(row);
+        const int sub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        o.tb[h] = row * D + 8 * (sub ^ (fr & 3)) + 4 * (lane & 1);
+        o.tx[h] = 32 * (fr >> 2);
+    }
+    return o;
+}
+
 // ------------------------------------------------------------------ tile maps
 struct BwdTile {
     int b, h;            // batch (sequence) and head (query head, or K/V head)
@@ -111,7 +150,7 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
 // Workgroup: 4 waves, 128 queries of one (b, h); K/V blocks of 64 keys.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
-    constexpr int BN = 64;
+    constexpr int BN = 32;
     constexpr int NDS = D / 16, NDT = D / 32, NKT = BN / 32, NKS = BN / 16;
     constexpr int TILE = BN * D;                       // elements of a K or V block
     constexpr int CH = TILE / 8 / kBwdThreads;         // 16-byte chunks per thread per block
@@ -209,20 +248,9 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
         }
     };
 
-    // Row-read offsets (A operand, 32 keys x 16 dims: key lq, chunk 2ds+g) and
-    // transpose-read offsets (K^T operand, as the forward's V^T).
-    int r_off[NDS];
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) r_off[ds] = lq * D + (((2 * ds + g) ^ vswz<D>(lq)) << 3);
-    int t_off[NDT][2];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 4 * g + ((lane & 15) >> 2) + 8 * h;
-            const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            t_off[dt][h] = row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
-        }
+    // Row reads (A operand, 32 keys x 16 dims: key lq, chunk 2ds+g) and
+    // transpose reads (K^T operand, as the forward's V^T).
+    LdsOffsets lo = lds_offsets<D>(lane);
 
     if (nblocks > 0) {
         load(0);
@@ -233,9 +261,11 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
             if (kb + 1 < nblocks) load(kb + 1);
             const unsigned short *Ks = smem + buf * TILE;
             const unsigned short *Vs = smem + (2 + buf) * TILE;
-            // Uniform per wave: does any of its rows see a key of this block?
-            const bool live = q0 < Nq && (!CAUSAL || kb * BN <= min(q0 + 31, Nq - 1) + shift);
-            if (live) {
+            lo.refresh();
+            // Every wave runs every block: a wave none of whose rows sees a key of
+            // this block gets dS = 0 from the mask (a branch here would split the
+            // accumulators' live ranges and cost register copies every block).
+            {
                 // S^T = K Q^T and dP^T = V dO^T for the 64 keys (32 per tile kt;
                 // 32-row tiles are 32 rows apart in the swizzled layout: the
                 // swizzle depends on the row within 16, unchanged by +32).
@@ -248,8 +278,8 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
                 for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
                     for (int kt = 0; kt < NKT; ++kt) {
-                        const bf16x8 kf = *(const bf16x8 *)(Ks + r_off[ds] + 32 * kt * D);
-                        const bf16x8 vf = *(const bf16x8 *)(Vs + r_off[ds] + 32 * kt * D);
+                        const bf16x8 kf = *(const bf16x8 *)(Ks + lo.row(ds) + 32 * kt * D);
+                        const bf16x8 vf = *(const bf16x8 *)(Vs + lo.row(ds) + 32 * kt * D);
                         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt], 0, 0, 0);
                         dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[ds], dp[kt], 0, 0, 0);
                     }
@@ -283,9 +313,9 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
                         const unsigned short *a0 = Ks + 16 * ks * D;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + t_off[dt][0]));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + t_off[dt][1]));
-                        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const i16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + lo.tr(dt, 0)));
+                        const i16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + lo.tr(dt, 1)));
+                        const i16x8 both = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
                         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
                                                                           sf[ks], acc[dt], 0, 0, 0);
                     }
@@ -313,15 +343,16 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------------ dK, dV kernel
 // Workgroup: 4 waves, 128 keys of one (b, K/V head); query blocks of 32.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int BQ = 32;
     constexpr int NDS = D / 16, NDT = D / 32, NQS = BQ / 16;
     constexpr int TILE = BQ * D;                       // elements of a Q or dO block
     constexpr int CH = TILE / 8 / kBwdThreads;         // 16-byte chunks per thread per block
     static_assert(CH >= 1, "block must cover the threads");
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE];
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE + 128 * D];
     __shared__ __attribute__((aligned(16))) float rowt[2][2][BQ];   // [buf][lse2, D][query]
-    // Q block in buffer b at smem + b * TILE, dO block at smem + (2 + b) * TILE.
+    // Q block in buffer b at smem + b * TILE, dO block at smem + (2 + b) * TILE,
+    // the workgroup's 128 V rows at smem + 4 * TILE (read as B operands of dP).
 
     BwdTile tc;
     if (!bwd_decode(blockIdx.x, p, p.Hkv, p.Nk, tc)) return;   // tc.h is the K/V head
@@ -339,18 +370,29 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     const unsigned short *Kg = (const unsigned short *)p.k + ktok * tkv + tc.h * D;
     const unsigned short *Vg = (const unsigned short *)p.v + ktok * tkv + tc.h * D;
 
-    // K and V fragments (B operands of S = Q K^T and dP = dO V^T, one key per lane).
-    bf16x8 kf[NDS], vf[NDS];
+    // K fragments in registers (B operands of S = Q K^T, one key per lane); the
+    // V rows of the workgroup go to LDS once (B operands of dP = dO V^T are read
+    // from there each block: holding them too would not fit two waves per SIMD).
+    bf16x8 kf[NDS];
+    unsigned short *Vs = smem + 4 * TILE;
     {
         const int rows = max(0, min(32, Nk - k0w));
         const unsigned bytes = rows > 0 ? (unsigned)(rows - 1) * tkvb + (unsigned)(D * 2) : 0u;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)k0w * tkv, bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)k0w * tkv, bytes);
         const unsigned off = (unsigned)lq * tkvb + (unsigned)(16 * g);
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
+        for (int ds = 0; ds < NDS; ++ds)
             kf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off + 32u * ds));
-            vf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rv, off + 32u * ds));
+        const int vrows = max(0, min(128, Nk - tc.m * 128));
+        const unsigned vbytes = vrows > 0 ? (unsigned)(vrows - 1) * tkvb + (unsigned)(D * 2) : 0u;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)tc.m * 128 * tkv, vbytes);
+        constexpr int VCH = 128 * D / 8 / kBwdThreads;
+#pragma unroll
+        for (int rr = 0; rr < VCH; ++rr) {
+            const int u = tid + kBwdThreads * rr;
+            const int row = u / (D / 8), cc = u % (D / 8);
+            const u32x4 x = buffer_load16(rv, (unsigned)row * tkvb + 16u * cc);
+            *(u32x4 *)(Vs + row * D + ((cc ^ vswz<D>(row)) << 3)) = x;
         }
     }
     const float c = p.scale_log2;
@@ -366,7 +408,6 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     int qb0 = 0;
     if (CAUSAL) qb0 = max(0, kfirst - shift) / BQ;
     const int nqb = (Nq + BQ - 1) / BQ;
-    const bool wave_live = key - lq < Nk;   // the wave has at least one key
 
     unsigned ld_off[CH];
     int st_off[CH];
@@ -378,8 +419,12 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
         st_off[rr] = row * D + ((cc ^ vswz<D>(row)) << 3);
     }
     u32x4 qreg[CH], oreg[CH];
-    float treg = 0.f;   // lse2 (threads 0..31) or D (threads 32..63) of one row
-    int cur_h = 0;
+    // One row term per lane of the first wave: LSE (lanes 0..31, scaled by
+    // log2 e when stored) or D (lanes 32..63) of query qb*BQ + lane % 32.  The
+    // loads are range-checked (0 past the sequence) and their values are not
+    // touched until the store, so the block's loads stay in flight meanwhile.
+    float tl = 0.f, td = 0.f;
+    const int64_t T = p.offsets ? (int64_t)p.offsets[p.B] : 0;
     auto load = [&](int h, int qb) {
         const unsigned short *Qg = (const unsigned short *)p.q + qtok * tq + h * D;
         const unsigned short *Og = (const unsigned short *)p.dout + qtok * tq + h * D;
@@ -392,16 +437,20 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             qreg[rr] = buffer_load16(rq, ld_off[rr]);
             oreg[rr] = buffer_load16(ro, ld_off[rr]);
         }
-        if (tid < 2 * BQ) {
-            const int i = qb * BQ + (tid & (BQ - 1));
-            float v = 0.f;
-            if (i < Nq) {
-                int64_t idx;
-                if (p.offsets) idx = (int64_t)h * p.offsets[p.B] + tc.tok0 + i;
-                else           idx = ((int64_t)tc.b * p.H + h) * Nq + i;
-                v = tid < BQ ? p.lse[idx] * 1.4426950408889634f : p.dsum[idx];
-            }
-            treg = v;
+        if (w == 0) {
+            const int64_t row0 = p.offsets ? (int64_t)h * T + tc.tok0
+                                           : ((int64_t)tc.b * p.H + h) * Nq;
+            const unsigned nb = rem > 0 ? (unsigned)min(rem, BQ) * 4u : 0u;
+            const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + row0 + (int64_t)qb * BQ, nb);
+            const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dsum + row0 + (int64_t)qb * BQ, nb);
+            // Both descriptors are uniform; each half of the wave reads one of
+            // them, the other load is out of range and returns 0.
+            const unsigned off = (unsigned)(lane & (BQ - 1)) * 4u;
+            const unsigned far = 0x7FFFFFF0u;
+            tl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rl, lane < BQ ? off : far, 0, 0));
+            td = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rd, lane < BQ ? far : off, 0, 0));
         }
     };
     auto store = [&](int buf) {
@@ -410,27 +459,16 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             *(u32x4 *)(smem + buf * TILE + st_off[rr]) = qreg[rr];
             *(u32x4 *)(smem + (2 + buf) * TILE + st_off[rr]) = oreg[rr];
         }
-        if (tid < 2 * BQ) rowt[buf][tid / BQ][tid & (BQ - 1)] = treg;
+        if (w == 0)
+            rowt[buf][lane / BQ][lane & (BQ - 1)] = lane < BQ ? tl * 1.4426950408889634f : td;
     };
 
-    int r_off[NDS];
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) r_off[ds] = lq * D + (((2 * ds + g) ^ vswz<D>(lq)) << 3);
-    int t_off[NDT][2];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 4 * g + ((lane & 15) >> 2) + 8 * h;
-            const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            t_off[dt][h] = row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
-        }
+    LdsOffsets lo = lds_offsets<D>(lane);
 
     const int steps_per_head = nqb - qb0;
     const int nsteps = steps_per_head > 0 ? steps_per_head * p.group : 0;
     if (nsteps > 0) {
-        cur_h = tc.h * p.group;
-        load(cur_h, qb0);
+        load(tc.h * p.group, qb0);
         store(0);
         __syncthreads();
         for (int st = 0; st < nsteps; ++st) {
@@ -442,19 +480,21 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             (void)h;
             const unsigned short *Qs = smem + buf * TILE;
             const unsigned short *Os = smem + (2 + buf) * TILE;
+            lo.refresh();
             const int qfirst = qb * BQ;
-            // Does this wave have a valid (query, key) pair in the block?
-            const bool live = wave_live && (!CAUSAL || qfirst + BQ - 1 + shift >= k0w);
-            if (live) {
+            // Every wave runs every block; pairs outside the mask get P = dS = 0.
+            {
                 f32x16 s, dp;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
 #pragma unroll
                 for (int ds = 0; ds < NDS; ++ds) {
-                    const bf16x8 qa = *(const bf16x8 *)(Qs + r_off[ds]);
-                    const bf16x8 oa = *(const bf16x8 *)(Os + r_off[ds]);
+                    const bf16x8 qa = *(const bf16x8 *)(Qs + lo.row(ds));
+                    const bf16x8 oa = *(const bf16x8 *)(Os + lo.row(ds));
+                    // V row 32w + lq: same swizzle as row lq (it depends on row % 16).
+                    const bf16x8 vb = *(const bf16x8 *)(Vs + 32 * w * D + lo.row(ds));
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[ds], dp, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dp, 0, 0, 0);
                 }
                 // Accumulator: lane = key, register i = query 8(i/4) + 4g + i%4.
                 // P and dS, masked pairs -> 0, to bf16 B operands (16 queries each).
@@ -497,10 +537,10 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
                     for (int dt = 0; dt < NDT; ++dt) {
                         const unsigned short *o0 = Os + 16 * qs * D;
                         const unsigned short *q0p = Qs + 16 * qs * D;
-                        const i16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(o0 + t_off[dt][0]));
-                        const i16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(o0 + t_off[dt][1]));
-                        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(q0p + t_off[dt][0]));
-                        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(q0p + t_off[dt][1]));
+                        const i16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(o0 + lo.tr(dt, 0)));
+                        const i16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(o0 + lo.tr(dt, 1)));
+                        const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(q0p + lo.tr(dt, 0)));
+                        const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(q0p + lo.tr(dt, 1)));
                         const i16x8 ob = __builtin_shufflevector(olo, ohi, 0, 1, 2, 3, 4, 5, 6, 7);
                         const i16x8 qbv = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
                         dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ob),
