@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_forward_fa_amd/csrc/fa_fwd_kernel.hip",
+                  "flashattention_forward_fa_amd/csrc/fa_device.h",
                   "flashattention_forward_fa_amd/csrc/fa_internal.h"]
 
 

@@ -36,6 +36,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -125,13 +127,21 @@ struct BwdTile {
     int L_q, L_k;        // query and key lengths of the sequence
 };
 
-// Tiles of 128 rows along a sequence: (b, h, m) from the workgroup index t,
-// linear order.  heads = the head count of the owning dimension.
+// Tiles of 128 rows along a sequence: (b, h, m) from the workgroup index t.
+// heads = the head count of the owning dimension.  The order is tile-position
+// major, every (b, h) at one position before the next, so that with causal
+// masking the heaviest tiles start first (longest-processing-time order): the
+// dQ tile m visits m + 1 key tiles' worth of blocks (reverse = true walks m
+// from the top), the dK/dV tile m visits the query blocks from m to the end
+// (reverse = false).  For packed sequences of unequal length the order is by
+// position only.
 __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads, int len_max,
-                                           BwdTile &c) {
+                                           bool reverse, BwdTile &c) {
     const int nm = (len_max + 127) / 128;
-    c.m = t % nm;
-    const int bh = t / nm;
+    const int nbh = p.B * heads;
+    c.m = t / nbh;
+    if (reverse) c.m = nm - 1 - c.m;
+    const int bh = t % nbh;
     c.b = bh / heads;
     c.h = bh % heads;
     if (p.offsets) {
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     // K block in buffer b at smem + b * TILE, V block at smem + (2 + b) * TILE.
 
     BwdTile tc;
-    if (!bwd_decode(blockIdx.x, p, p.H, p.Nq, tc)) return;
+    if (!bwd_decode(blockIdx.x, p, p.H, p.Nq, CAUSAL, tc)) return;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
@@ -283,30 +293,41 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
                         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt], 0, 0, 0);
                         dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[ds], dp[kt], 0, 0, 0);
                     }
-                // dS^T = P^T (dP^T - D), masked keys -> 0; to bf16 B operands.
+                // dS^T = P^T (dP^T - D), masked keys -> 0; to bf16 B operands.  A
+                // block every pair of which is kept skips the test (wave-uniform).
                 const int kv0 = kb * BN;
                 const int lim = row_ok ? (CAUSAL ? min(Nk - 1, qrow + shift) : Nk - 1) - kv0 - 4 * g
                                        : -(1 << 30);
+                const bool full = q0 + 31 < Nq && kv0 + BN - 1 < Nk &&
+                                  (!CAUSAL || kv0 + BN - 1 <= q0 + shift);
                 bf16x8 sf[NKS];
+                auto frags = [&](auto masked) {
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    unsigned wd[4];
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        unsigned wd[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float v2[2];
+                        for (int e = 0; e < 4; ++e) {
+                            float v2[2];
 #pragma unroll
-                        for (int h2 = 0; h2 < 2; ++h2) {
-                            const int i = 8 * (ks & 1) + 2 * e + h2;
-                            const int kt = ks >> 1;
-                            const int key = 32 * kt + 8 * (i >> 2) + (i & 3);   // relative to kv0 + 4g
-                            const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -lse2));
-                            v2[h2] = key > lim ? 0.f : pr * (dp[kt][i] - dsum);
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                const int i = 8 * (ks & 1) + 2 * e + h2;
+                                const int kt = ks >> 1;
+                                const int key = 32 * kt + 8 * (i >> 2) + (i & 3);   // relative to kv0 + 4g
+                                const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -lse2));
+                                const float v = pr * (dp[kt][i] - dsum);
+                                if constexpr (decltype(masked)::value)
+                                    v2[h2] = key > lim ? 0.f : v;
+                                else
+                                    v2[h2] = v;
+                            }
+                            wd[e] = pack_bf16x2(v2[0], v2[1]);
                         }
-                        wd[e] = pack_bf16x2(v2[0], v2[1]);
+                        const u32x4 x = {wd[0], wd[1], wd[2], wd[3]};
+                        sf[ks] = __builtin_bit_cast(bf16x8, x);
                     }
-                    const u32x4 x = {wd[0], wd[1], wd[2], wd[3]};
-                    sf[ks] = __builtin_bit_cast(bf16x8, x);
-                }
+                };
+                if (full) frags(std::false_type{});
+                else      frags(std::true_type{});
                 // dQ^T += K^T dS^T.
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
@@ -355,7 +376,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     // the workgroup's 128 V rows at smem + 4 * TILE (read as B operands of dP).
 
     BwdTile tc;
-    if (!bwd_decode(blockIdx.x, p, p.Hkv, p.Nk, tc)) return;   // tc.h is the K/V head
+    if (!bwd_decode(blockIdx.x, p, p.Hkv, p.Nk, false, tc)) return;   // tc.h is the K/V head
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
