@@ -517,14 +517,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ds], s, 0, 0, 0);
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vb, dp, 0, 0, 0);
                 }
-                // Accumulator: lane = key, register i = query 8(i/4) + 4g + i%4.
-                // P and dS, masked pairs -> 0, to bf16 B operands (16 queries each).
+                // Accumulator: lane = key, register i = query qfirst + 4g + qo(i) with
+                // qo(i) = 8(i/4) + i%4.  P and dS are formed for every pair and packed
+                // to bf16 B operands (16 queries each); then, only in a block that the
+                // mask cuts (wave-uniform test), the dropped pairs are zeroed in the
+                // packed words: a pair is kept iff mlo <= qo < mhi (query in the
+                // sequence, key in the sequence and, when causal, not after the query).
+                // Values formed for dropped pairs may be inf or NaN; the select
+                // replaces their bits without reading them as numbers.
                 const float4 *lrow = (const float4 *)rowt[buf][0];
                 const float4 *drow = (const float4 *)rowt[buf][1];
-                bf16x8 pfr[NQS], sfr[NQS];
+                u32x4 pwv[NQS], swv[NQS];
 #pragma unroll
                 for (int qs = 0; qs < NQS; ++qs) {
-                    unsigned pw[4], sw[4];
 #pragma unroll
                     for (int hh = 0; hh < 2; ++hh) {
                         const int i0 = 8 * qs + 4 * hh;         // registers i0..i0+3
@@ -535,21 +540,38 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                         float pv[4], sv[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int qi = qfirst + 8 * ((i0 + e) >> 2) + 4 * g + e;
-                            const bool ok = key < Nk && qi < Nq && (!CAUSAL || key <= qi + shift);
-                            const float pr = __builtin_amdgcn_exp2f(fmaf(s[i0 + e], c, -lv[e]));
-                            pv[e] = ok ? pr : 0.f;
+                            pv[e] = __builtin_amdgcn_exp2f(fmaf(s[i0 + e], c, -lv[e]));
                             sv[e] = pv[e] * (dp[i0 + e] - dvv[e]);
                         }
-                        pw[2 * hh] = pack_bf16x2(pv[0], pv[1]);
-                        pw[2 * hh + 1] = pack_bf16x2(pv[2], pv[3]);
-                        sw[2 * hh] = pack_bf16x2(sv[0], sv[1]);
-                        sw[2 * hh + 1] = pack_bf16x2(sv[2], sv[3]);
+                        pwv[qs][2 * hh] = pack_bf16x2(pv[0], pv[1]);
+                        pwv[qs][2 * hh + 1] = pack_bf16x2(pv[2], pv[3]);
+                        swv[qs][2 * hh] = pack_bf16x2(sv[0], sv[1]);
+                        swv[qs][2 * hh + 1] = pack_bf16x2(sv[2], sv[3]);
                     }
-                    const u32x4 xp = {pw[0], pw[1], pw[2], pw[3]};
-                    const u32x4 xs = {sw[0], sw[1], sw[2], sw[3]};
-                    pfr[qs] = __builtin_bit_cast(bf16x8, xp);
-                    sfr[qs] = __builtin_bit_cast(bf16x8, xs);
+                }
+                const bool full = k0w + 31 < Nk && qfirst + BQ - 1 < Nq &&
+                                  (!CAUSAL || k0w + 31 <= qfirst + shift);
+                if (!full) {
+                    const int qbase = qfirst + 4 * g;
+                    const int mhi = Nq - qbase;
+                    const int mlo = key >= Nk ? (1 << 30) : (CAUSAL ? key - shift - qbase : -(1 << 30));
+#pragma unroll
+                    for (int qs = 0; qs < NQS; ++qs)
+#pragma unroll
+                        for (int wd = 0; wd < 4; ++wd) {
+                            const int r = 8 * qs + 4 * (wd >> 1) + 2 * (wd & 1);   // registers r, r + 1
+                            const int qa = 8 * (r >> 2) + (r & 3), qb = qa + 1;
+                            const unsigned keep = ((qa >= mlo && qa < mhi) ? 0x0000FFFFu : 0u) |
+                                                  ((qb >= mlo && qb < mhi) ? 0xFFFF0000u : 0u);
+                            pwv[qs][wd] &= keep;
+                            swv[qs][wd] &= keep;
+                        }
+                }
+                bf16x8 pfr[NQS], sfr[NQS];
+#pragma unroll
+                for (int qs = 0; qs < NQS; ++qs) {
+                    pfr[qs] = __builtin_bit_cast(bf16x8, pwv[qs]);
+                    sfr[qs] = __builtin_bit_cast(bf16x8, swv[qs]);
                 }
                 // dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transpose reads).
 #pragma unroll
