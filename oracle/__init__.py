@@ -88,6 +88,11 @@ class Oracle:
                                                              ctypes.c_int64, ctypes.c_int64,
                                                              ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_bwd_varlen.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        lib.oracle_attn_bwd_rows.argtypes = [_F64P] * 4 + [i64, i64, i64, i64, ctypes.c_double,
+                                                           ctypes.c_int, i64, _I64P, _F64P, i64,
+                                                           _I64P, _F64P, _F64P]
+        lib.oracle_attn_bwd_rows.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -206,6 +211,30 @@ class Oracle:
             raise RuntimeError("oracle_attn_bwd_varlen failed")
         return dq, dk, dv
 
+    def attention_bwd_rows(self, q, k, v, dout, scale: float, causal: bool, qrows, krows):
+        """Selected gradient rows of one (batch, K/V head) with its G query heads.
+
+        q, dout [Nq,G,d]; k, v [Nk,d]; qrows: (g, i) pairs; krows: key indices.
+        Returns (dq [len(qrows),d], dk [len(krows),d], dv [len(krows),d])."""
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        if q.ndim != 3 or k.ndim != 2 or k.shape != v.shape or dout.shape != q.shape or \
+                k.shape[1] != q.shape[2]:
+            raise ValueError("expected q, dout [Nq,G,d] and k, v [Nk,d]")
+        Nq, G, d = q.shape
+        Nk = k.shape[0]
+        qr = np.ascontiguousarray(np.asarray(qrows, dtype=np.int64).reshape(-1, 2))
+        kr = np.ascontiguousarray(np.asarray(krows, dtype=np.int64).reshape(-1))
+        dq = np.zeros((qr.shape[0], d))
+        dk = np.zeros((kr.shape[0], d))
+        dv = np.zeros((kr.shape[0], d))
+        rc = self.lib.oracle_attn_bwd_rows(_p(q), _p(k), _p(v), _p(dout), G, Nq, Nk, d,
+                                           float(scale), int(bool(causal)), qr.shape[0],
+                                           _p(qr, _I64P), _p(dq), kr.shape[0], _p(kr, _I64P),
+                                           _p(dk), _p(dv))
+        if rc != 0:
+            raise RuntimeError("oracle_attn_bwd_rows failed (bad row index or allocation)")
+        return dq, dk, dv
+
 
 def default() -> Oracle:
     """The oracle built from oracle.c in this directory (built on first use)."""
@@ -233,3 +262,7 @@ def attention_bwd(q, k, v, dout, scale: float, causal: bool):
 
 def attention_bwd_varlen(q, k, v, dout, offsets, scale: float, causal: bool):
     return default().attention_bwd_varlen(q, k, v, dout, offsets, scale, causal)
+
+
+def attention_bwd_rows(q, k, v, dout, scale: float, causal: bool, qrows, krows):
+    return default().attention_bwd_rows(q, k, v, dout, scale, causal, qrows, krows)

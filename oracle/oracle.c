@@ -412,3 +412,128 @@ int oracle_attn_bwd_varlen(const double *q, const double *k, const double *v, co
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Selected rows of the gradients, for checks at sizes where the full
+ * gradients are too slow here.  One (batch or sequence, K/V head) with its G
+ * query heads: q, dout [Nq, G, d]; k, v [Nk, d] (contiguous slices).  Same
+ * definitions as above ("FlashAttention-4（下）", section 1), taken in order:
+ *
+ *   1. for every query row (g, i): LSE_gi = ln sum_j exp(s_gij) and
+ *      D_gi = sum_j P_gij dP_gij over its valid keys;
+ *   2. dQ for the requested rows (g, i): scale * sum_j P_gij (dP_gij - D_gi) k_j;
+ *   3. dK, dV for the requested key rows j, summed over the G query heads and
+ *      the queries that see key j: dV_j = sum P_gij dO_gi,
+ *      dK_j = scale * sum P_gij (dP_gij - D_gi) q_gi.
+ *
+ * qrows holds nq pairs (g, i); krows holds nk key indices; dq_out [nq, d],
+ * dk_out, dv_out [nk, d].  Returns -1 on a bad argument or allocation failure.
+ */
+int oracle_attn_bwd_rows(const double *q, const double *k, const double *v, const double *dout,
+                         int64_t G, int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                         int64_t nq, const int64_t *qrows, double *dq_out,
+                         int64_t nk, const int64_t *krows, double *dk_out, double *dv_out)
+{
+    if (!q || !k || !v || !dout || G <= 0 || Nq < 0 || Nk < 0 || d <= 0 || nq < 0 || nk < 0 ||
+        (nq > 0 && (!qrows || !dq_out)) || (nk > 0 && (!krows || !dk_out || !dv_out)))
+        return -1;
+    for (int64_t r = 0; r < nq; ++r)
+        if (qrows[2 * r] < 0 || qrows[2 * r] >= G || qrows[2 * r + 1] < 0 || qrows[2 * r + 1] >= Nq)
+            return -1;
+    for (int64_t r = 0; r < nk; ++r)
+        if (krows[r] < 0 || krows[r] >= Nk) return -1;
+    const int64_t rs = G * d;                       /* token stride of q and dout */
+    double *lse = (double *)malloc(sizeof(double) * (size_t)(G * Nq > 0 ? G * Nq : 1));
+    double *dsum = (double *)malloc(sizeof(double) * (size_t)(G * Nq > 0 ? G * Nq : 1));
+    if (!lse || !dsum) {
+        free(lse);
+        free(dsum);
+        return -1;
+    }
+    int bad = 0;
+    /* 1. per query row: LSE and D */
+#pragma omp parallel
+    {
+        double *s_buf = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        if (!s_buf) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t u = 0; u < G * Nq; ++u) {
+                const int64_t g = u / Nq, i = u % Nq;
+                const double *qi = q + i * rs + g * d, *doi = dout + i * rs + g * d;
+                const int64_t nvalid = valid_keys(i, Nq, Nk, causal);
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nvalid; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c) dot += qi[c] * k[j * d + c];
+                    s_buf[j] = scale * dot;
+                    if (s_buf[j] > m) m = s_buf[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < nvalid; ++j) l += exp(s_buf[j] - m);
+                const double L = nvalid > 0 ? m + log(l) : -INFINITY;
+                double D = 0.0;
+                for (int64_t j = 0; j < nvalid; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c) dot += doi[c] * v[j * d + c];
+                    D += exp(s_buf[j] - L) * dot;
+                }
+                lse[u] = L;
+                dsum[u] = D;
+            }
+        }
+        free(s_buf);
+    }
+    if (bad) {
+        free(lse);
+        free(dsum);
+        return -1;
+    }
+    /* 2. dQ rows */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nq; ++r) {
+        const int64_t g = qrows[2 * r], i = qrows[2 * r + 1];
+        const double *qi = q + i * rs + g * d, *doi = dout + i * rs + g * d;
+        double *out = dq_out + r * d;
+        for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+        const int64_t nvalid = valid_keys(i, Nq, Nk, causal);
+        for (int64_t j = 0; j < nvalid; ++j) {
+            double sd = 0.0, pd = 0.0;
+            for (int64_t c = 0; c < d; ++c) {
+                sd += qi[c] * k[j * d + c];
+                pd += doi[c] * v[j * d + c];
+            }
+            const double p = exp(scale * sd - lse[g * Nq + i]);
+            const double ds = p * (pd - dsum[g * Nq + i]);
+            for (int64_t c = 0; c < d; ++c) out[c] += scale * ds * k[j * d + c];
+        }
+    }
+    /* 3. dK, dV rows */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nk; ++r) {
+        const int64_t j = krows[r];
+        double *ok = dk_out + r * d, *ov = dv_out + r * d;
+        for (int64_t c = 0; c < d; ++c) ok[c] = ov[c] = 0.0;
+        for (int64_t g = 0; g < G; ++g)
+            for (int64_t i = 0; i < Nq; ++i) {
+                if (j >= valid_keys(i, Nq, Nk, causal)) continue;
+                const double *qi = q + i * rs + g * d, *doi = dout + i * rs + g * d;
+                double sd = 0.0, pd = 0.0;
+                for (int64_t c = 0; c < d; ++c) {
+                    sd += qi[c] * k[j * d + c];
+                    pd += doi[c] * v[j * d + c];
+                }
+                const double p = exp(scale * sd - lse[g * Nq + i]);
+                const double ds = p * (pd - dsum[g * Nq + i]);
+                for (int64_t c = 0; c < d; ++c) {
+                    ov[c] += p * doi[c];
+                    ok[c] += scale * ds * qi[c];
+                }
+            }
+    }
+    free(lse);
+    free(dsum);
+    return 0;
+}

@@ -531,10 +531,33 @@ def pin_bwd_varlen_is_per_sequence(orc):
                 _close(g[sl], w[0], what=f"{name} seq {b}")
 
 
+def pin_bwd_rows_torch_autograd(orc):
+    """Selected gradient rows (one batch entry, one K/V head with its G query heads) vs
+    torch's fp64 autograd of SDPA, including Nq != Nk, causal rows without keys and G > 1."""
+    rng = np.random.default_rng(32)
+    for (Nq, Nk, G, d, causal) in [(7, 7, 1, 4, True), (5, 9, 3, 6, True), (9, 4, 2, 5, True),
+                                   (6, 8, 2, 3, False)]:
+        q = rng.standard_normal((1, Nq, G, d))
+        k = rng.standard_normal((1, Nk, 1, d))
+        v = rng.standard_normal((1, Nk, 1, d))
+        do = rng.standard_normal((1, Nq, G, d))
+        want = _torch_grads(q, k, v, do, 0.61, causal)
+        qrows = [(g, i) for g in range(G) for i in range(Nq)]
+        krows = list(range(Nk))[::-1]
+        dq, dk, dv = orc.attention_bwd_rows(q[0], k[0, :, 0], v[0, :, 0], do[0], 0.61, causal,
+                                            qrows, krows)
+        for r, (g, i) in enumerate(qrows):
+            _close(dq[r], want[0][0, i, g], tol=1e-12, what=f"dQ row {(g, i)} {Nq, Nk, G, causal}")
+        for r, j in enumerate(krows):
+            _close(dk[r], want[1][0, j, 0], tol=1e-12, what=f"dK row {j} {Nq, Nk, G, causal}")
+            _close(dv[r], want[2][0, j, 0], tol=1e-12, what=f"dV row {j} {Nq, Nk, G, causal}")
+
+
 ALL_PINS = [pin_worked_example, pin_causal_figure12, pin_bottom_right_alignment,
             pin_exercise7_bounds, pin_torch_sdpa, pin_rows_sum_to_one, pin_shift_invariance,
             pin_causal_row0, pin_convex_hull, pin_future_independence, pin_scale_zero_mean,
             pin_rows_without_keys, pin_key_permutation, pin_head_batch_slices,
             pin_varlen_is_per_sequence, pin_rows_match_full, pin_torch_sdpa_grouped_heads,
             pin_gqa_exercise8, pin_gqa_equals_repeated_heads, pin_bwd_torch_autograd,
-            pin_bwd_finite_differences, pin_bwd_invariants, pin_bwd_varlen_is_per_sequence]
+            pin_bwd_finite_differences, pin_bwd_invariants, pin_bwd_varlen_is_per_sequence,
+            pin_bwd_rows_torch_autograd]

@@ -59,14 +59,18 @@ def ref_bwd(w, dout_bits):
     return oracle.attention_bwd(q, k, v, do, w.scale, w.causal)
 
 
-def compare_grads(got, ref, what):
+def compare_grads(got, ref, what, extra=(0.0, 0.0, 0.0)):
+    """extra: per-gradient allowance at four standard deviations, added to the
+    element bound, and at one (a quarter of it) to the mean bound -- the
+    row-term allowance of the full-size dQ checks; 0 elsewhere."""
     stats = {}
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+    for name, g, r, ex in zip(("dQ", "dK", "dV"), got, ref, extra):
         assert g.shape == r.shape, f"{what} {name} shape"
         assert np.all(np.isfinite(g)), f"{what} {name} not finite"
         rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
         err = np.abs(g - r)
-        bound = 2.0 ** -7 * np.abs(r) + 0.05 * rms + 1e-5
+        ex = np.broadcast_to(np.asarray(ex, dtype=np.float64), r.shape)
+        bound = 2.0 ** -7 * np.abs(r) + 0.05 * rms + 1e-5 + ex
         stats[name] = dict(max_err=float(err.max(initial=0.0)), rms=rms,
                            max_over_rms=float(err.max(initial=0.0) / rms) if rms else 0.0,
                            mean_over_rms=float(err.mean() / rms) if rms and err.size else 0.0)
@@ -77,7 +81,8 @@ def compare_grads(got, ref, what):
                                  f"(ref {r[idx]:.4f}, got {g[idx]:.4f}, rms {rms:.3e}); "
                                  f"{int(bad.sum())} elements")
         if rms:
-            assert err.mean() <= 3e-3 * rms, f"{what} {name}: mean error {err.mean():.3e} vs rms {rms:.3e}"
+            assert err.mean() <= 3e-3 * rms + 0.25 * ex.mean(), \
+                f"{what} {name}: mean error {err.mean():.3e} vs rms {rms:.3e} (+{0.25 * ex.mean():.3e})"
     return stats
 
 
@@ -136,3 +141,95 @@ def test_bwd_deterministic():
     b = run_bwd(w, do)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def _sample(n, rng, count, block=128):
+    """Row indices: first/last, the edges of every 128-row tile (capped), and random rows."""
+    edges = sorted({0, n - 1} | {x for t in range(0, n, block) for x in (t, t + block - 1) if x < n})
+    if len(edges) > 48:
+        edges = edges[:24] + edges[-24:]
+    extra = rng.integers(0, n, count) if n > 0 else np.zeros(0, dtype=np.int64)
+    return sorted(set(edges) | {int(x) for x in extra})
+
+
+FULL_SIZE = ["2", "3", "4", "5", "3-kv8"]
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_bwd_full_size_sampled(name):
+    """The measured workloads at full size, in the launch the benchmark times
+    (fa_bwd on the forward's O and LSE, dO from seed + 500); the oracle computes
+    sampled dQ rows and dK, dV rows of two (batch or sequence, K/V head) slices.
+
+    Row-term allowance for dQ.  The GPU forms D_i = dO_i . O_i from the
+    forward's bf16 O, whose elements differ from the exact O by their bf16
+    rounding (up to 2^-9 |O|) plus the forward's own error (mean 2.6e-4,
+    measured); an error dD_i moves every dS_ij of the row by -P_ij dD_i and so
+    dQ_i by -scale dD_i Kbar_i with Kbar_i = sum_j P_ij k_j.  The d per-element
+    errors are independent, so dD_i is taken at four standard deviations of
+    their sum, 4 sqrt(sum_c dO_ic^2 (2^-9 |O_ic| + 3e-4)^2), and the allowance
+    for element (i, c) is scale dD_i |Kbar_ic|; O_i and Kbar_i come from the
+    oracle's forward (Kbar_i is attention with V := K).  It matters where one
+    key dominates a row and that key is large: the outlier keys of the
+    N = 16384 workload (8x scaled rows) make Kbar large exactly there.
+
+    The same errors reach dK_j = scale sum_i dS_ij q_i as -scale sum_i P_ij dD_i
+    q_i, a sum of independent terms over the queries (of all G heads) that see
+    key j; its allowance is four standard deviations,
+    4 scale sqrt(sum_i P_ij^2 sigma_i^2 q_ic^2) with sigma_i the one-sigma dD_i
+    above, and P_ij = exp(scale q_i.k_j - LSE_i) from the oracle's LSE.  It
+    matters for the first keys of a causal sequence, which every query sees
+    and which carry most of the weight of the short rows."""
+    w = wl.grouped(3, 8) if name == "3-kv8" else wl.config(int(name))
+    dout = wl.make_dout(w, seed=w.seed + 500)
+    dq, dk, dv = run_bwd(w, dout)
+    G = w.H // w.kv_heads
+    rng = np.random.default_rng(4242 + len(name))
+    if w.varlen:
+        order = np.argsort(w.lengths)
+        slices = [(int(order[-1]), 0), (int(order[len(order) // 2]), w.kv_heads - 1)]
+    else:
+        slices = [(0, 0), (w.B - 1, w.kv_heads - 1)]
+    for (b, kvh) in slices:
+        hs = slice(kvh * G, (kvh + 1) * G)
+        if w.varlen:
+            t = slice(int(w.offsets[b]), int(w.offsets[b + 1]))
+            sel = lambda x, hsl: x[t, hsl]
+        else:
+            sel = lambda x, hsl: x[b, :, hsl]
+        q = wl.bf16_to_f64(sel(w.q, hs))
+        k = wl.bf16_to_f64(sel(w.k, kvh))
+        v = wl.bf16_to_f64(sel(w.v, kvh))
+        do = wl.bf16_to_f64(sel(dout, hs))
+        Nq, Nk = q.shape[0], k.shape[0]
+        qi = _sample(Nq, rng, 48)
+        qrows = [(g, i) for i in qi for g in range(G)]
+        krows = _sample(Nk, rng, 48)
+        rq, rk, rv = oracle.attention_bwd_rows(q, k, v, do, w.scale, w.causal, qrows, krows)
+        rows3 = [(0, g, i) for (g, i) in qrows]
+        o_ref, _ = oracle.attention_rows(q[None], k[None, :, None], v[None, :, None], w.scale,
+                                         w.causal, rows3)
+        kbar, _ = oracle.attention_rows(q[None], k[None, :, None], k[None, :, None], w.scale,
+                                        w.causal, rows3)
+        do_rows = np.stack([do[i, g] for (g, i) in qrows])
+        dD = 4.0 * np.sqrt(np.sum((do_rows * (2.0 ** -9 * np.abs(o_ref) + 3e-4)) ** 2, axis=1))
+        allow_q = abs(w.scale) * dD[:, None] * np.abs(kbar)
+        o_all, lse_all = oracle.attention(q[None], k[None, :, None], v[None, :, None], w.scale,
+                                          w.causal)
+        sig = np.sqrt(np.sum((do * (2.0 ** -9 * np.abs(o_all[0]) + 3e-4)) ** 2, axis=2))  # [Nq,G]
+        kr = np.asarray(krows)
+        sc = w.scale * np.einsum("igc,jc->igj", q, k[kr])
+        seen = np.ones((Nq, kr.size), dtype=bool)
+        if w.causal:
+            seen = kr[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)
+        lse_t = lse_all[0].T[:, :, None]                                    # [Nq,G,1]
+        pr = np.where(seen[:, None, :], np.exp(np.where(seen[:, None, :], sc - lse_t, -np.inf)), 0.0)
+        allow_k = 4.0 * abs(w.scale) * np.sqrt(np.einsum("igj,igc->jc", (pr * sig[:, :, None]) ** 2,
+                                                         q ** 2))
+        gq = np.stack([sel(dq, hs)[i, g] for (g, i) in qrows])
+        gk = np.stack([sel(dk, kvh)[j] for j in krows])
+        gv = np.stack([sel(dv, kvh)[j] for j in krows])
+        stats = compare_grads((gq, gk, gv), (rq, rk, rv), f"{w.name} slice {(b, kvh)}",
+                              extra=(allow_q, allow_k, 0.0))
+        stats["dQ"]["mean_allowance_over_rms"] = float(0.25 * allow_q.mean() / stats["dQ"]["rms"])
+        print(w.name, (b, kvh), stats)

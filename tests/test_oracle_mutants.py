@@ -37,6 +37,8 @@ MUTANTS = {
     "bwd_dk_from_dq_side": ("dk[j * kstride + c] += scale * ds * qi[c];", "dk[j * kstride + c] += scale * ds * doi[c];"),
     "bwd_kv_head_modulo": ("for (int64_t h = kvh * group; h < (kvh + 1) * group; ++h)\n                    bwd_head(q + (b * Nq * H + h) * d",
                            "for (int64_t h = kvh; h < H; h += Hkv)\n                    bwd_head(q + (b * Nq * H + h) * d"),
+    "bwd_rows_dk_from_dout": ("ok[c] += scale * ds * qi[c];", "ok[c] += scale * ds * doi[c];"),
+    "bwd_rows_row_term_unweighted": ("D += exp(s_buf[j] - L) * dot;", "D += dot;"),
     "lse_wrong_slot": ("lse + (b * H + h) * Nq + i);", "lse + (h * B + b) * Nq + i);"),
 }
 
