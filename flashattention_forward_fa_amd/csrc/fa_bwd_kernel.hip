@@ -24,12 +24,19 @@
 //   dP^T = V dO^T with one query per lane (Q and dO fragments in registers),
 //   dS^T in bf16 as the B operand of dQ^T += K^T dS^T, K^T by transpose reads.
 // * The key-block kernel is its transpose: S = Q K^T and dP = dO V^T with one
-//   key per lane (K and V fragments in registers); P and dS in bf16 are the B
-//   operands of dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T by transpose
-//   reads.  The per-query LSE and D come from LDS, four rows per 16-byte read.
+//   key per lane (K fragments in registers, the workgroup's V rows in LDS); P
+//   and dS in bf16 are the B operands of dV^T += dO^T P and dK^T += Q^T dS, dO^T
+//   and Q^T by transpose reads.  The per-query LSE and D come from LDS, four
+//   rows per 16-byte read.
 // * Tiles in LDS use the swizzled layout of fa_device.h, free of bank
 //   conflicts for both the 16-byte row reads and the transpose reads.  Blocks
 //   are double-buffered through registers with one barrier per block.
+// * Register budget: two waves per SIMD (at most 256 VGPRs each; the library
+//   is built with MFMA accumulators in ordinary VGPRs).  The dK/dV wave holds
+//   128 accumulator registers, 32 of K, 32 of S and dP and the block staging;
+//   hence V from LDS, the LDS read offsets kept as two registers per family
+//   (LdsOffsets) and no branch around the products (a per-wave branch there
+//   splits the accumulators' live ranges and costs copies every block).
 // * Grouped K/V heads: the key-block kernel of K/V head kv walks the query
 //   heads kv*G .. kv*G+G-1 in turn and writes dK, dV once.
 #include <hip/hip_runtime.h>
@@ -157,7 +164,8 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
 }
 
 // ------------------------------------------------------------------ dQ kernel
-// Workgroup: 4 waves, 128 queries of one (b, h); K/V blocks of 64 keys.
+// Workgroup: 4 waves, 128 queries of one (b, h); K/V blocks of 32 keys (64 would
+// not fit two waves per SIMD: S and dP of 64 keys alone take 64 registers).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int BN = 32;
