@@ -5,7 +5,8 @@
 // for one (batch, head), with the forward's LSE and the upstream gradient dO,
 //
 //   P_ij  = exp(scale * q_i.k_j - LSE_i)          (recomputed, masked -> 0)
-//   D_i   = dO_i . O_i                            (pre-pass, one value per row)
+//   D_i   = dO_i . O_i                            (one value per row, formed by
+//                                                  the dQ kernel, kept for dK/dV)
 //   dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i)
 //   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 //
@@ -52,40 +53,6 @@ namespace fa {
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
-
-// ------------------------------------------------------------------ pre-pass
-// D_i = sum_c dO_ic O_ic in fp32 for every row (b, h, i); layout of LSE.
-// Each row is handled by D/8 lanes (16 bytes each), reduced by lane exchange.
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_dsum_kernel(BwdParams p) {
-    constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int RPB = 256 / CPR;             // rows per workgroup
-    const int tid = threadIdx.x;
-    const int64_t row = (int64_t)blockIdx.x * RPB + tid / CPR;   // token-major: (token, head)
-    const int c = tid % CPR;
-    const int64_t T = p.offsets ? (int64_t)p.offsets[p.B] : (int64_t)p.B * p.Nq;
-    float acc = 0.f;
-    const bool ok = row < T * p.H;
-    if (ok) {
-        const u32x4 a = *(const u32x4 *)((const unsigned short *)p.dout + row * D + 8 * c);
-        const u32x4 b = *(const u32x4 *)((const unsigned short *)p.o + row * D + 8 * c);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
-            acc = fmaf(__uint_as_float(a[e] & 0xFFFF0000u), __uint_as_float(b[e] & 0xFFFF0000u), acc);
-        }
-    }
-#pragma unroll
-    for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-    if (ok && c == 0) {
-        const int64_t t = row / p.H;
-        const int h = (int)(row % p.H);
-        int64_t idx;
-        if (p.offsets) idx = (int64_t)h * T + t;
-        else           idx = ((t / p.Nq) * p.H + h) * (int64_t)p.Nq + t % p.Nq;
-        p.dsum[idx] = acc;
-    }
-}
 
 // ------------------------------------------------------------------ LDS offsets
 // A lane's swizzled read offsets (elements) into a row-major D-wide tile, each
@@ -192,6 +159,7 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     const int64_t ktok = (p.offsets ? tc.tok0 : (int64_t)tc.b * p.Nk);
     const unsigned short *Qg = (const unsigned short *)p.q + qtok * tq + tc.h * D;
     const unsigned short *dOg = (const unsigned short *)p.dout + qtok * tq + tc.h * D;
+    const unsigned short *Og_in = (const unsigned short *)p.o + qtok * tq + tc.h * D;
     const unsigned short *Kg = (const unsigned short *)p.k + ktok * tkv + hkv * D;
     const unsigned short *Vg = (const unsigned short *)p.v + ktok * tkv + hkv * D;
 
@@ -203,28 +171,42 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
         nblocks = kmax < 0 ? 0 : min(nblocks, kmax / BN + 1);
     }
 
-    // Q and dO fragments (B operands, one query per lane) and the row terms.
+    // Q and dO fragments (B operands, one query per lane: this lane holds the
+    // 16-byte chunks 2ds + g of its row) and the row terms.  D_i = dO_i . O_i is
+    // formed here from the same chunks of O, the two half-waves' parts added by
+    // one lane exchange, and stored for the dK/dV kernel, which runs after this
+    // one on the stream.
     bf16x8 qf[NDS], of[NDS];
+    float dpart = 0.f;
     {
         const int rows = max(0, min(32, Nq - q0));
         const unsigned bytes = rows > 0 ? (unsigned)(rows - 1) * tqb + (unsigned)(D * 2) : 0u;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + (int64_t)q0 * tq, bytes);
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOg + (int64_t)q0 * tq, bytes);
+        const __amdgpu_buffer_rsrc_t rO = make_rsrc(Og_in + (int64_t)q0 * tq, bytes);
         const unsigned off = (unsigned)lq * tqb + (unsigned)(16 * g);
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
             qf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rq, off + 32u * ds));
-            of[ds] = __builtin_bit_cast(bf16x8, buffer_load16(ro, off + 32u * ds));
+            const u32x4 dov = buffer_load16(ro, off + 32u * ds);
+            const u32x4 ov = buffer_load16(rO, off + 32u * ds);
+            of[ds] = __builtin_bit_cast(bf16x8, dov);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dpart = fmaf(__uint_as_float(dov[e] << 16), __uint_as_float(ov[e] << 16), dpart);
+                dpart = fmaf(__uint_as_float(dov[e] & 0xFFFF0000u), __uint_as_float(ov[e] & 0xFFFF0000u), dpart);
+            }
         }
     }
+    const float dsum = dpart + __shfl_xor(dpart, 32, 64);
     const float c = p.scale_log2;
-    float lse2 = 0.f, dsum = 0.f;
+    float lse2 = 0.f;
     if (row_ok) {
         int64_t idx;
         if (p.offsets) idx = (int64_t)tc.h * p.offsets[p.B] + tc.tok0 + qrow;
         else           idx = ((int64_t)tc.b * p.H + tc.h) * Nq + qrow;
         lse2 = p.lse[idx] * 1.4426950408889634f;
-        dsum = p.dsum[idx];
+        if (g == 0) p.dsum[idx] = dsum;
     }
 
     f32x16 acc[NDT];
@@ -625,9 +607,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
 template <int D>
 static int launch_bwd_d(const BwdParams &p, bool causal, hipStream_t s) {
-    const int64_t rows = (int64_t)p.B * p.Nq * p.H;          // upper bound for varlen
-    const int rpb = 256 / (D / 8);
-    hipLaunchKernelGGL((fa_bwd_dsum_kernel<D>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, s, p);
     const unsigned gq = (unsigned)((int64_t)p.B * p.H * ((p.Nq + 127) / 128));
     const unsigned gk = (unsigned)((int64_t)p.B * p.Hkv * ((p.Nk + 127) / 128));
     if (causal) {
