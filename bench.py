@@ -18,8 +18,8 @@ Prints one JSON line:
   cpu_baseline the fp64 CPU oracle timed on a bounded sample of the same
                workload (whole (batch, head) slices until ~10 s have passed)
 
-With --backward a step is one fa_bwd call (three launches: the row term
-D = rowsum(dO*O), the dQ kernel, the dK/dV kernel) on the forward's O and LSE
+With --backward a step is one fa_bwd call (two launches: the dQ kernel, which
+also forms the row terms D = rowsum(dO*O), then the dK/dV kernel) on the forward's O and LSE
 and a seeded dO; its flops are counted as 2.5x the forward's (the five
 products of the gradient), the events bracket the whole call, and traffic is
 null.
