@@ -53,6 +53,7 @@ namespace fa {
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;   // query (dQ) or key (dK/dV) rows per workgroup
 
 // ------------------------------------------------------------------ LDS offsets
 // A lane's swizzled read offsets (elements) into a row-major D-wide tile, each
@@ -101,7 +102,7 @@ struct BwdTile {
     int L_q, L_k;        // query and key lengths of the sequence
 };
 
-// Tiles of 128 rows along a sequence: (b, h, m) from the workgroup index t.
+// Tiles of kBwdRows rows along a sequence: (b, h, m) from the workgroup index t.
 // heads = the head count of the owning dimension.  The order is tile-position
 // major, every (b, h) at one position before the next, so that with causal
 // masking the heaviest tiles start first (longest-processing-time order): the
@@ -111,7 +112,7 @@ struct BwdTile {
 // position only.
 __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads, int len_max,
                                            bool reverse, BwdTile &c) {
-    const int nm = (len_max + 127) / 128;
+    const int nm = (len_max + kBwdRows - 1) / kBwdRows;
     const int nbh = p.B * heads;
     c.m = t / nbh;
     if (reverse) c.m = nm - 1 - c.m;
@@ -122,7 +123,7 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
         c.tok0 = p.offsets[c.b];
         c.L_q = c.L_k = p.offsets[c.b + 1] - c.tok0;
         const int len = c.L_q;
-        return c.m * 128 < len;
+        return c.m * kBwdRows < len;
     }
     c.tok0 = 0;
     c.L_q = p.Nq;
@@ -138,7 +139,9 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int BN = 32;
     constexpr int NDS = D / 16, NDT = D / 32, NKT = BN / 32, NKS = BN / 16;
     constexpr int TILE = BN * D;                       // elements of a K or V block
-    constexpr int CH = TILE / 8 / kBwdThreads;         // 16-byte chunks per thread per block
+    constexpr int NCHUNK = TILE / 8;                   // 16-byte chunks per block
+    constexpr int CH = (NCHUNK + kBwdThreads - 1) / kBwdThreads;   // ... per thread
+    constexpr bool EXACT = NCHUNK % kBwdThreads == 0;  // else the last round is partial
     __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE];
     // K block in buffer b at smem + b * TILE, V block at smem + (2 + b) * TILE.
 
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
     const int Nq = tc.L_q, Nk = tc.L_k;
     const int shift = Nk - Nq;
-    const int q0 = tc.m * 128 + 32 * w;                // first query of this wave
+    const int q0 = tc.m * kBwdRows + 32 * w;           // first query of this wave
     const int qrow = q0 + lq;
     const bool row_ok = qrow < Nq;
     const int hkv = tc.h / p.group;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     // Keys this tile visits.
     int nblocks = (Nk + BN - 1) / BN;
     if (CAUSAL) {
-        const int last_row = min(tc.m * 128 + 128, Nq) - 1;
+        const int last_row = min(tc.m * kBwdRows + kBwdRows, Nq) - 1;
         const int kmax = last_row + shift;
         nblocks = kmax < 0 ? 0 : min(nblocks, kmax / BN + 1);
     }
@@ -215,14 +218,15 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
-    // Cooperative block loads: chunk u = tid + 256 * rr of a 64 x D block.
+    // Cooperative block loads: chunk u = tid + kBwdThreads * rr of a BN x D
+    // block (a chunk past the block reads out of range, is 0 and is not stored).
     unsigned ld_off[CH];
     int st_off[CH];
 #pragma unroll
     for (int rr = 0; rr < CH; ++rr) {
         const int u = tid + kBwdThreads * rr;
         const int row = u / (D / 8), cc = u % (D / 8);
-        ld_off[rr] = (unsigned)row * tkvb + 16u * cc;
+        ld_off[rr] = (EXACT || u < NCHUNK) ? (unsigned)row * tkvb + 16u * cc : 0x7FFFFFF0u;
         st_off[rr] = row * D + ((cc ^ vswz<D>(row)) << 3);
     }
     u32x4 kreg[CH], vreg[CH];
@@ -243,6 +247,7 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     auto store = [&](int buf) {
 #pragma unroll
         for (int rr = 0; rr < CH; ++rr) {
+            if (!EXACT && tid + kBwdThreads * rr >= NCHUNK) continue;
             *(u32x4 *)(smem + buf * TILE + st_off[rr]) = kreg[rr];
             *(u32x4 *)(smem + (2 + buf) * TILE + st_off[rr]) = vreg[rr];
         }
@@ -358,12 +363,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     constexpr int BQ = 32;
     constexpr int NDS = D / 16, NDT = D / 32, NQS = BQ / 16;
     constexpr int TILE = BQ * D;                       // elements of a Q or dO block
-    constexpr int CH = TILE / 8 / kBwdThreads;         // 16-byte chunks per thread per block
-    static_assert(CH >= 1, "block must cover the threads");
-    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE + 128 * D];
+    constexpr int NCHUNK = TILE / 8;                   // 16-byte chunks per block
+    constexpr int CH = (NCHUNK + kBwdThreads - 1) / kBwdThreads;   // ... per thread
+    constexpr bool EXACT = NCHUNK % kBwdThreads == 0;  // else the last round is partial
+    __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE + kBwdRows * D];
     __shared__ __attribute__((aligned(16))) float rowt[2][2][BQ];   // [buf][lse2, D][query]
     // Q block in buffer b at smem + b * TILE, dO block at smem + (2 + b) * TILE,
-    // the workgroup's 128 V rows at smem + 4 * TILE (read as B operands of dP).
+    // the workgroup's V rows at smem + 4 * TILE (read as B operands of dP).
 
     BwdTile tc;
     if (!bwd_decode(blockIdx.x, p, p.Hkv, p.Nk, false, tc)) return;   // tc.h is the K/V head
@@ -372,7 +378,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
     const int Nq = tc.L_q, Nk = tc.L_k;
     const int shift = Nk - Nq;
-    const int k0w = tc.m * 128 + 32 * w;               // first key of this wave
+    const int k0w = tc.m * kBwdRows + 32 * w;          // first key of this wave
     const int key = k0w + lq;
     const int64_t tq = (int64_t)p.H * D, tkv = (int64_t)p.Hkv * D;
     const unsigned tqb = (unsigned)(tq * 2), tkvb = (unsigned)(tkv * 2);
@@ -394,10 +400,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds)
             kf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off + 32u * ds));
-        const int vrows = max(0, min(128, Nk - tc.m * 128));
+        const int vrows = max(0, min(kBwdRows, Nk - tc.m * kBwdRows));
         const unsigned vbytes = vrows > 0 ? (unsigned)(vrows - 1) * tkvb + (unsigned)(D * 2) : 0u;
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)tc.m * 128 * tkv, vbytes);
-        constexpr int VCH = 128 * D / 8 / kBwdThreads;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)tc.m * kBwdRows * tkv, vbytes);
+        constexpr int VCH = kBwdRows * D / 8 / kBwdThreads;
 #pragma unroll
         for (int rr = 0; rr < VCH; ++rr) {
             const int u = tid + kBwdThreads * rr;
@@ -415,7 +421,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.f; dv[dt][i] = 0.f; }
 
     // Query blocks this key tile meets: causal rows i with i + shift >= first key.
-    const int kfirst = tc.m * 128;
+    const int kfirst = tc.m * kBwdRows;
     int qb0 = 0;
     if (CAUSAL) qb0 = max(0, kfirst - shift) / BQ;
     const int nqb = (Nq + BQ - 1) / BQ;
@@ -426,7 +432,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     for (int rr = 0; rr < CH; ++rr) {
         const int u = tid + kBwdThreads * rr;
         const int row = u / (D / 8), cc = u % (D / 8);
-        ld_off[rr] = (unsigned)row * tqb + 16u * cc;
+        ld_off[rr] = (EXACT || u < NCHUNK) ? (unsigned)row * tqb + 16u * cc : 0x7FFFFFF0u;
         st_off[rr] = row * D + ((cc ^ vswz<D>(row)) << 3);
     }
     u32x4 qreg[CH], oreg[CH];
@@ -467,6 +473,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     auto store = [&](int buf) {
 #pragma unroll
         for (int rr = 0; rr < CH; ++rr) {
+            if (!EXACT && tid + kBwdThreads * rr >= NCHUNK) continue;
             *(u32x4 *)(smem + buf * TILE + st_off[rr]) = qreg[rr];
             *(u32x4 *)(smem + (2 + buf) * TILE + st_off[rr]) = oreg[rr];
         }
@@ -607,8 +614,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
 
 template <int D>
 static int launch_bwd_d(const BwdParams &p, bool causal, hipStream_t s) {
-    const unsigned gq = (unsigned)((int64_t)p.B * p.H * ((p.Nq + 127) / 128));
-    const unsigned gk = (unsigned)((int64_t)p.B * p.Hkv * ((p.Nk + 127) / 128));
+    const unsigned gq = (unsigned)((int64_t)p.B * p.H * ((p.Nq + kBwdRows - 1) / kBwdRows));
+    const unsigned gk = (unsigned)((int64_t)p.B * p.Hkv * ((p.Nk + kBwdRows - 1) / kBwdRows));
     if (causal) {
         hipLaunchKernelGGL((fa_bwd_dq_kernel<D, true>), dim3(gq), dim3(kBwdThreads), 0, s, p);
         hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, true>), dim3(gk), dim3(kBwdThreads), 0, s, p);
