@@ -69,6 +69,18 @@ def traffic_from_profile(workload: str):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float, backward: bool = False):
     """Time the oracle on whole (sequence, head) slices of the workload until budget_s
     (the backward: gradients of one slice's O for the seeded dO)."""
@@ -113,7 +125,7 @@ def cpu_baseline(w, budget_s: float, backward: bool = False):
     # The backward's parallel loop runs over (batch, K/V head): one slice per call is
     # one thread.  The forward's runs over query rows and uses every thread.
     cores = 1 if backward else orc.num_threads()
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": cores,
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": cores, "cpu": cpu_model(),
             "kind": "oracle",
             "sample": f"{done} of {len(units)} (sequence, head) slices, every query row of each, "
                       f"{what}, {spent:.1f} s"}
