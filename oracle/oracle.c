@@ -464,16 +464,16 @@ int oracle_attn_bwd_rows(const double *q, const double *k, const double *v, cons
                 const int64_t g = u / Nq, i = u % Nq;
                 const double *qi = q + i * rs + g * d, *doi = dout + i * rs + g * d;
                 const int64_t nvalid = valid_keys(i, Nq, Nk, causal);
-                double m = -INFINITY;
+                double mrow = -INFINITY;
                 for (int64_t j = 0; j < nvalid; ++j) {
-                    double dot = 0.0;
-                    for (int64_t c = 0; c < d; ++c) dot += qi[c] * k[j * d + c];
-                    s_buf[j] = scale * dot;
-                    if (s_buf[j] > m) m = s_buf[j];
+                    double qk = 0.0;
+                    for (int64_t c = 0; c < d; ++c) qk += qi[c] * k[j * d + c];
+                    s_buf[j] = scale * qk;
+                    if (s_buf[j] > mrow) mrow = s_buf[j];
                 }
-                double l = 0.0;
-                for (int64_t j = 0; j < nvalid; ++j) l += exp(s_buf[j] - m);
-                const double L = nvalid > 0 ? m + log(l) : -INFINITY;
+                double lrow = 0.0;
+                for (int64_t j = 0; j < nvalid; ++j) lrow += exp(s_buf[j] - mrow);
+                const double L = nvalid > 0 ? mrow + log(lrow) : -INFINITY;
                 double D = 0.0;
                 for (int64_t j = 0; j < nvalid; ++j) {
                     double dot = 0.0;
