@@ -38,11 +38,11 @@ int check_args(const void *q, const void *k, const void *v, const void *o, const
         if (Nq != Nk) return FA_ERR_INVALID_ARG;   // packed sequences attend to themselves
     }
     // Tile count and element offsets must fit the kernel's integer arithmetic.
-    const int64_t num_m = ((int64_t)Nq + fa::kBlockM - 1) / fa::kBlockM;
+    const int64_t num_m = ((int64_t)Nq + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
     if ((int64_t)B * H * num_m >= (int64_t)1 << 31) return FA_ERR_INVALID_ARG;
     // Byte offsets inside a tile's buffer descriptors are 32-bit: a 256-row
-    // Q/O tile spans 256 * H * d * 2 bytes.
-    if ((int64_t)fa::kBlockM * H * d * 2 >= (int64_t)1 << 32) return FA_ERR_INVALID_ARG;
+    // Q/O tile spans 256 * H * d * 2 bytes (the same bound for every head size).
+    if ((int64_t)fa::kBlockMMax * H * d * 2 >= (int64_t)1 << 32) return FA_ERR_INVALID_ARG;
     if ((int64_t)B * Nq >= (int64_t)1 << 31 || (int64_t)B * Nk >= (int64_t)1 << 31)
         return FA_ERR_INVALID_ARG;
     return FA_OK;
@@ -156,7 +156,7 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
     p.Hkv = H / p.group;
     p.Nq = Nq;
     p.Nk = Nk;
-    p.num_m = (Nq + fa::kBlockM - 1) / fa::kBlockM;
+    p.num_m = (Nq + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
     p.num_tiles = B * H * p.num_m;
     const bool lpt_default = causal != 0;
     p.lpt = op.schedule == FA_SCHEDULE_LPT ? 1 : op.schedule == FA_SCHEDULE_LINEAR ? 0 : lpt_default;

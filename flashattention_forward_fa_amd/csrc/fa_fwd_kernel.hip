@@ -2,7 +2,7 @@
 //
 // What one workgroup computes ("Flash Attention 4", mlc.ai, section "algorithm
 // structure"; "FlashAttention：一次前向计算", qingsen, section "general update"):
-// for a tile of kBlockM query rows of one (batch, head) it walks the K/V blocks
+// for a tile of fwd_block_m(d) query rows of one (batch, head) it walks the K/V blocks
 // j = 0, 1, ... and keeps, per row, the exponent reference r, the running
 // denominator l and the unnormalised output o:
 //
@@ -46,6 +46,10 @@
 // * Ping-pong between the two waves of a SIMD (see the schedule below): one
 //   wave issues its MFMAs (S_j and O += P_{j-1} V_{j-1}) while the other
 //   runs its softmax on the VALU; workgroup barriers separate the phases.
+//   This is the d = 128 shape (8 waves, 256 rows, one workgroup per CU).  At
+//   d = 64 a workgroup is 4 waves (128 rows) with no phase offset and three
+//   workgroups share a CU: there the softmax outweighs the products and more
+//   independent waves issue more VALU work.
 // * K and V blocks are double-buffered in LDS, staged through registers with
 //   buffer loads (range-checked per block) one phase ahead.  K rows are
 //   padded by 16 bytes and V rows swizzled (chunk c of row r at c ^ f(r)), so
@@ -70,8 +74,9 @@ template <int D_>
 struct Tile {
     static constexpr int D = D_;
     static constexpr int BN = kBlockN;
-    static constexpr int NW = kWaves;
-    static constexpr int BM = kBlockM;
+    static constexpr int NW = fwd_waves(D_);
+    static constexpr int BM = fwd_block_m(D_);
+    static constexpr bool PINGPONG = NW == 8;   // two groups of 4 waves, one phase apart
     static constexpr int NT = 64 * NW;        // threads per workgroup
     static constexpr int KS = D + 8;          // K row stride in LDS (bf16 elements)
     static constexpr int K_ELEMS = BN * KS;
@@ -123,6 +128,7 @@ __device__ __forceinline__ bool decode_fixed(int t, const FwdParams &p, TileCoor
 // Varlen, longest first: all tiles with query-tile index m = num_m-1 come
 // first (every sequence long enough, in sequence order, heads innermost), then
 // m = num_m-2, ...  Computed per wave from the offsets, with no host sync.
+template <int BM>
 __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoord &c) {
     const int lane = threadIdx.x & 63;
     const int32_t *off = p.offsets;
@@ -134,7 +140,7 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
             for (int b0 = 0; b0 < p.B; b0 += 64) {
                 const int bb = b0 + lane;
                 int nblk = 0;
-                if (bb < p.B) nblk = (off[bb + 1] - off[bb] + kBlockM - 1) / kBlockM;
+                if (bb < p.B) nblk = (off[bb + 1] - off[bb] + BM - 1) / BM;
                 cnt += __popcll(__ballot(nblk > lvl));
             }
             const int tiles = cnt * p.H;
@@ -144,7 +150,7 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
                 for (int b0 = 0; b0 < p.B; b0 += 64) {
                     const int bb = b0 + lane;
                     int nblk = 0;
-                    if (bb < p.B) nblk = (off[bb + 1] - off[bb] + kBlockM - 1) / kBlockM;
+                    if (bb < p.B) nblk = (off[bb + 1] - off[bb] + BM - 1) / BM;
                     const unsigned long long mask = __ballot(nblk > lvl);
                     const int n = __popcll(mask);
                     if (target < n) {
@@ -167,7 +173,7 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
         b = bh / p.H;
         h = bh % p.H;
         const int L = off[b + 1] - off[b];
-        if (m * kBlockM >= L) return false;
+        if (m * BM >= L) return false;
     }
     const int start = off[b];
     const int L = off[b + 1] - start;
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     unsigned short *const Vbuf1 = smem + 2 * T::K_ELEMS + T::V_ELEMS;
 
     TileCoord tc;
-    const bool ok = VARLEN ? decode_varlen(blockIdx.x, p, tc) : decode_fixed(blockIdx.x, p, tc);
+    const bool ok = VARLEN ? decode_varlen<T::BM>(blockIdx.x, p, tc) : decode_fixed(blockIdx.x, p, tc);
     if (!ok) return;   // uniform over the workgroup
 
     const int tid = threadIdx.x;
@@ -277,18 +283,27 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     //   slot 2j+1: group 0 V(j)   group 1 M(j)
     //
     // K_b lives in Kbuf[b % 2], V_b in Vbuf[b % 2].  Group g loads its part
-    // of each block (K rows 32g..32g+31; V^T head-dim half g); in V(j) it
+    // of each block (K and V rows 32g..32g+31); in V(j) it
     // writes K_{j+1+g} and V_{j+g} (staged in registers one V phase earlier)
     // and issues the loads of K_{j+2+g} and V_{j+1+g}.  Every buffer is
     // written only after both groups' last reads of its previous block and
     // before the first read of the new one (one barrier apart).
+    //
+    // With 4 waves (d = 64) there is one group: M(j), V(j), barrier.  V(j)
+    // writes the buffers M(j-1) read, and the barrier after V(j-1) orders
+    // every wave's M(j-1) before any wave's V(j), so one barrier per block
+    // suffices; the overlap of MFMA and VALU work comes from the other
+    // workgroups on the CU.
     // ---------------------------------------------------------------------
-    const int grp = w >> 2;
-    const int gtid = tid & 255;
+    constexpr bool PP = T::PINGPONG;
+    const int grp = PP ? w >> 2 : 0;
+    const int gtid = PP ? tid & 255 : tid;
 
-    // Per-thread load/store coordinates for this group's part of a block.
-    constexpr int KPT2 = (32 * D / 8) / 256;        // 16-byte K chunks per thread
-    static_assert(KPT2 >= 1 && (32 * D / 8) % 256 == 0, "K half must split over 256 threads");
+    // Per-thread load/store coordinates for this group's part of a block
+    // (32 rows per group with the ping-pong, the whole block without).
+    constexpr int GROWS = PP ? 32 : T::BN;
+    constexpr int KPT2 = (GROWS * D / 8) / 256;     // 16-byte K chunks per thread
+    static_assert(KPT2 >= 1 && (GROWS * D / 8) % 256 == 0, "block part must split over 256 threads");
     unsigned k_voff[KPT2];
     int k_lds[KPT2];
 #pragma unroll
@@ -512,21 +527,32 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         unsigned short *const Vw_even = grp ? Vbuf1 : Vbuf0;
         unsigned short *const Kw_odd = grp ? Kbuf1 : Kbuf0;    // j odd
         unsigned short *const Vw_odd = grp ? Vbuf0 : Vbuf1;
-        if (grp == 1) {
-            v_phase(-1, Kw_odd, Vw_odd);
-            __syncthreads();
+        if constexpr (PP) {
+            if (grp == 1) {
+                v_phase(-1, Kw_odd, Vw_odd);
+                __syncthreads();
+            }
+            for (int j = 0; j <= n; j += 2) {
+                m_phase(j, Kbuf0, Vbuf1);
+                __syncthreads();
+                v_phase(j, Kw_even, Vw_even);
+                __syncthreads();
+                m_phase(j + 1, Kbuf1, Vbuf0);
+                __syncthreads();
+                v_phase(j + 1, Kw_odd, Vw_odd);
+                __syncthreads();
+            }
+            if (grp == 0) __syncthreads();
+        } else {
+            for (int j = 0; j <= n; j += 2) {
+                m_phase(j, Kbuf0, Vbuf1);
+                v_phase(j, Kw_even, Vw_even);
+                __syncthreads();
+                m_phase(j + 1, Kbuf1, Vbuf0);
+                v_phase(j + 1, Kw_odd, Vw_odd);
+                __syncthreads();
+            }
         }
-        for (int j = 0; j <= n; j += 2) {
-            m_phase(j, Kbuf0, Vbuf1);
-            __syncthreads();
-            v_phase(j, Kw_even, Vw_even);
-            __syncthreads();
-            m_phase(j + 1, Kbuf1, Vbuf0);
-            __syncthreads();
-            v_phase(j + 1, Kw_odd, Vw_odd);
-            __syncthreads();
-        }
-        if (grp == 0) __syncthreads();
     }
 
     // Epilogue: O = o / l, LSE = ln l + r * scale.

@@ -5,11 +5,14 @@
 
 namespace fa {
 
-// Tile shape of the forward kernel: a workgroup of kWaves wavefronts owns
-// kBlockM = 32 * kWaves query rows (32 per wave); K/V stream in blocks of
-// kBlockN keys.
-constexpr int kWaves = 8;
-constexpr int kBlockM = 32 * kWaves;
+// Tile shape of the forward kernel: a workgroup of fwd_waves(d) wavefronts
+// owns fwd_block_m(d) = 32 * fwd_waves(d) query rows (32 per wave); K/V stream
+// in blocks of kBlockN keys.  d = 128: 8 waves in two ping-pong groups, one
+// workgroup per CU.  d = 64: 4 waves in one group, three workgroups per CU
+// (the softmax-bound head size gains from more independent waves).
+constexpr int fwd_waves(int d) { return d == 64 ? 4 : 8; }
+constexpr int fwd_block_m(int d) { return 32 * fwd_waves(d); }
+constexpr int kBlockMMax = 256;   // the largest fwd_block_m (sizes its 32-bit offsets)
 constexpr int kBlockN = 64;
 constexpr int kNumXcd = 8;   // MI355X: 8 accelerator complex dies, one L2 each
 
