@@ -25,6 +25,7 @@ import pytest
 import oracle
 from flashattention_forward_fa_amd import workloads as wl
 from tests import parity
+from tests.parity import compare_grads
 
 pytestmark = pytest.mark.gpu
 
@@ -57,33 +58,6 @@ def ref_bwd(w, dout_bits):
     if w.varlen:
         return oracle.attention_bwd_varlen(q, k, v, do, w.offsets, w.scale, w.causal)
     return oracle.attention_bwd(q, k, v, do, w.scale, w.causal)
-
-
-def compare_grads(got, ref, what, extra=(0.0, 0.0, 0.0)):
-    """extra: per-gradient allowance at four standard deviations, added to the
-    element bound, and at one (a quarter of it) to the mean bound -- the
-    row-term allowance of the full-size dQ checks; 0 elsewhere."""
-    stats = {}
-    for name, g, r, ex in zip(("dQ", "dK", "dV"), got, ref, extra):
-        assert g.shape == r.shape, f"{what} {name} shape"
-        assert np.all(np.isfinite(g)), f"{what} {name} not finite"
-        rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
-        err = np.abs(g - r)
-        ex = np.broadcast_to(np.asarray(ex, dtype=np.float64), r.shape)
-        bound = 2.0 ** -7 * np.abs(r) + 0.05 * rms + 1e-5 + ex
-        stats[name] = dict(max_err=float(err.max(initial=0.0)), rms=rms,
-                           max_over_rms=float(err.max(initial=0.0) / rms) if rms else 0.0,
-                           mean_over_rms=float(err.mean() / rms) if rms and err.size else 0.0)
-        bad = err > bound
-        if bad.any():
-            idx = np.unravel_index(np.argmax(err - bound), err.shape)
-            raise AssertionError(f"{what} {name}: error {err[idx]:.3e} > {bound[idx]:.3e} at {idx} "
-                                 f"(ref {r[idx]:.4f}, got {g[idx]:.4f}, rms {rms:.3e}); "
-                                 f"{int(bad.sum())} elements")
-        if rms:
-            assert err.mean() <= 3e-3 * rms + 0.25 * ex.mean(), \
-                f"{what} {name}: mean error {err.mean():.3e} vs rms {rms:.3e} (+{0.25 * ex.mean():.3e})"
-    return stats
 
 
 SHAPES = [
