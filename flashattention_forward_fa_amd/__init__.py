@@ -40,7 +40,8 @@ class FaError(RuntimeError):
 class FaFwdOpts(ctypes.Structure):
     """Mirror of ``fa_fwd_opts`` in include/fa.h."""
     _fields_ = [("o_dtype", ctypes.c_int32), ("rescale_threshold", ctypes.c_float),
-                ("schedule", ctypes.c_int32), ("kv_heads", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("rescale_counts", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -153,14 +154,15 @@ def fa_version() -> int:
 
 def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_seqlen=None,
               o_dtype=FA_DTYPE_BF16, rescale_threshold: float = 8.0,
-              schedule: int = FA_SCHEDULE_AUTO, stream=None):
+              schedule: int = FA_SCHEDULE_AUTO, stream=None, rescale_counts: bool = False):
     """Allocate O and LSE with torch on q's device and run fa_fwd_ex.
 
     Fixed length: q [B,Nq,H,d], k/v [B,Nk,Hkv,d] bf16 -> o [B,Nq,H,d], lse [B,H,Nq].
     Varlen: q [T,H,d], k/v [T,Hkv,d] and int32 offsets [B+1] on the device,
     max_seqlen = the longest sequence -> o [T,H,d], lse [H,T].
     Hkv (read from k's shape) divides H; query heads h*G .. h*G+G-1, G = H/Hkv,
-    share K/V head h.
+    share K/V head h.  rescale_counts=True also returns each row's count of
+    rescale events (int32, laid out like lse): (o, lse, counts).
     """
     import torch
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
@@ -192,10 +194,14 @@ def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_s
     opts.rescale_threshold = rescale_threshold
     opts.schedule = schedule
     opts.kv_heads = Hkv
+    counts = None
+    if rescale_counts:
+        counts = torch.zeros(lse.shape, dtype=torch.int32, device=q.device)
+        opts.rescale_counts = counts.data_ptr()
     st = fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets, stream, opts)
     if st != FA_OK:
         raise FaError(st, "fa_fwd_ex")
-    return o, lse
+    return (o, lse, counts) if rescale_counts else (o, lse)
 
 
 def attention_bwd(q, k, v, o, lse, dout, scale: float, causal: bool, *, varlen_offsets=None,

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;   // 0.3.0: backward pass
+constexpr int kVersion = 400;   // 0.4.0: per-row rescale counts (fa_fwd_opts.rescale_counts)
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -31,6 +31,7 @@ int check_args(const void *q, const void *k, const void *v, const void *o, const
     if (opts.schedule < FA_SCHEDULE_AUTO || opts.schedule > FA_SCHEDULE_LPT) return FA_ERR_INVALID_ARG;
     if (opts.kv_heads < 0 || opts.kv_heads > H || (opts.kv_heads > 0 && H % opts.kv_heads != 0))
         return FA_ERR_INVALID_ARG;
+    if ((uintptr_t)opts.rescale_counts & 3u) return FA_ERR_INVALID_ARG;
     if (opts.o_dtype != FA_DTYPE_BF16 && opts.o_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (offsets) {
@@ -53,9 +54,7 @@ int check_bwd(const void *q, const void *k, const void *v, const void *o, const 
               int B, int H, int Nq, int Nk, int d, float scale, int causal,
               const int32_t *offsets, int kv_heads) {
     fa_fwd_opts opts;
-    opts.o_dtype = FA_DTYPE_BF16;
-    opts.rescale_threshold = 8.0f;
-    opts.schedule = FA_SCHEDULE_AUTO;
+    fa_fwd_opts_default(&opts);
     opts.kv_heads = kv_heads;
     const int st = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, offsets, opts);
     if (st != FA_OK) return st;
@@ -123,6 +122,7 @@ void fa_fwd_opts_default(fa_fwd_opts *opts) {
     opts->rescale_threshold = 8.0f;
     opts->schedule = FA_SCHEDULE_AUTO;
     opts->kv_heads = 0;
+    opts->rescale_counts = nullptr;
 }
 
 int fa_fwd_check(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -176,6 +176,7 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
         p.scale_log2 = 1.0f;
     }
     p.threshold = op.rescale_threshold;
+    p.rescale_counts = op.rescale_counts;
 
     // Clear a stale error so the status below belongs to this launch.
     (void)hipGetLastError();

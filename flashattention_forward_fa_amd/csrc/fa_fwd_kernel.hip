@@ -188,7 +188,7 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
 }
 
 // ------------------------------------------------------------------ kernel
-template <int D, bool CAUSAL, bool VARLEN, typename OutT>
+template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT>
 __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     using T = Tile<D>;
     __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::K_ELEMS + 2 * T::V_ELEMS];
@@ -263,6 +263,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
 
+    unsigned nmoves = 0;     // COUNT: reference moves after the row's first live block
     float r = -INFINITY;     // exponent reference (unscaled score units)
     float lsum = 0.f;        // this lane's half of the row sum of bf16(P) (normalises O)
     float lsum32 = 0.f;      // ... of the fp32 P (gives LSE)
@@ -452,6 +453,7 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         const bool first = r == -INFINITY;
         const float delta = first ? -INFINITY : (r - cand) * c;
         const bool move = live && !(delta >= -tau);
+        if constexpr (COUNT) nmoves += (move && !first) ? 1u : 0u;
         alpha = move ? __builtin_amdgcn_exp2f(delta) : 1.f;
         r = move ? cand : r;
         const float neg_rc = (r == -INFINITY) ? 0.f : -r * c;
@@ -582,14 +584,19 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
             if (VARLEN) idx = (int64_t)tc.h * p.offsets[p.B] + tc.q_tok0 + qrow;
             else        idx = ((int64_t)tc.b * p.H + tc.h) * Nq + qrow;
             p.lse[idx] = lse;
+            if constexpr (COUNT) p.rescale_counts[idx] = nmoves;
         }
     }
 }
 
 template <int D, bool CAUSAL, bool VARLEN, typename OutT>
 static int launch_one(const FwdParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT>), dim3(p.num_tiles),
-                       dim3(Tile<D>::NT), 0, stream, p);
+    if (p.rescale_counts)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, true>), dim3(p.num_tiles),
+                           dim3(Tile<D>::NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, false>), dim3(p.num_tiles),
+                           dim3(Tile<D>::NT), 0, stream, p);
     return (int)hipGetLastError();
 }
 

@@ -36,6 +36,7 @@ struct FwdParams {
     float scale;              // |s|, used for LSE
     float scale_log2;         // exponent scale: |s| * log2(e) rounded once (1 when s = 0)
     float threshold;          // tau
+    uint32_t *rescale_counts; // nullptr, or per-row counts of reference moves (layout of lse)
 };
 
 // Enqueue the forward kernel; returns a hipError_t value (0 = success).

@@ -94,15 +94,27 @@ typedef enum fa_schedule {
  *   schedule          : fa_schedule (default FA_SCHEDULE_AUTO).
  *   kv_heads          : number of K/V heads Hkv; 0 (the default) means H,
  *                       otherwise 1 <= Hkv <= H and Hkv divides H.
+ *   rescale_counts    : NULL (the default), or device memory, 4-byte aligned,
+ *                       of one uint32 per query row laid out like lse
+ *                       ([B, H, Nq], or [H, T] for varlen), owned by the caller.
+ *                       When given, each row's count of rescale events is
+ *                       written: the K/V blocks after the row's first one with a
+ *                       valid key at which its exponent reference moved
+ *                       ("Flash Attention 4", section "algorithm structure":
+ *                       delta < -tau).  Diagnostics: the computation and the
+ *                       other outputs are the same; without it the kernels
+ *                       carry no counting code.
  */
 typedef struct fa_fwd_opts {
     int32_t o_dtype;
     float rescale_threshold;
     int32_t schedule;
     int32_t kv_heads;
+    uint32_t *rescale_counts;
 } fa_fwd_opts;
 
-/* Fill *opts with the defaults (bf16 O, tau = 8, automatic schedule, Hkv = H). */
+/* Fill *opts with the defaults (bf16 O, tau = 8, automatic schedule, Hkv = H,
+ * no rescale counts). */
 void fa_fwd_opts_default(fa_fwd_opts *opts);
 
 /*

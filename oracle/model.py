@@ -34,12 +34,19 @@ import numpy as np
 
 
 def fa4_forward(q, k, v, scale: float, causal: bool = False, block_n: int = 128,
-                threshold: float = 8.0, reverse: bool = False, trace: bool = False):
-    """One head: q [Nq, d], k/v [Nk, d] -> dict(o, lse, rescales, trace).
+                threshold: float = 8.0, reverse: bool = False, trace: bool = False,
+                tie_eps: float = 1e-3):
+    """One head: q [Nq, d], k/v [Nk, d] -> dict(o, lse, rescales, rescale_rows,
+    near_ties, trace).
 
     ``threshold`` is tau (8 = conditional rescale, 0 = always rescale);
     ``reverse`` walks the K/V blocks from last to first.  ``rescales`` counts
-    (row, block) pairs where the reference was switched after the first block.
+    (row, block) pairs where the reference was switched after the first block;
+    ``rescale_rows`` is that count per row, and ``near_ties`` per row the number
+    of such later blocks whose decision was within ``tie_eps`` of the threshold:
+    the decision compares the block's maximum with the reference, so the margin
+    is |(row_max - block max) * scale_log2 + threshold| (both finite); there an
+    fp32 evaluation of the same scores may decide the other way.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -53,6 +60,8 @@ def fa4_forward(q, k, v, scale: float, causal: bool = False, block_n: int = 128,
     O = np.zeros((Nq, v.shape[1]))
     first = True
     rescales = 0
+    rescale_rows = np.zeros(Nq, dtype=np.int64)
+    near_ties = np.zeros(Nq, dtype=np.int64)
     states = []
 
     nblocks = (Nk + block_n - 1) // block_n
@@ -76,6 +85,12 @@ def fa4_forward(q, k, v, scale: float, causal: bool = False, block_n: int = 128,
             with np.errstate(invalid="ignore"):
                 acc_scale = np.where(keep, 1.0, np.exp2(np.where(keep, 0.0, delta)))
             rescales += int(np.count_nonzero(~keep))
+            rescale_rows += ~keep
+            bmax = S.max(axis=1)
+            both = np.isfinite(row_max) & np.isfinite(bmax)
+            with np.errstate(invalid="ignore"):
+                gap = np.where(both, (row_max - bmax) * scale_log2, np.inf)
+            near_ties += both & (np.abs(gap + threshold) < tie_eps)
         row_max_safe = np.where(new_ref == -np.inf, 0.0, new_ref)
         P = np.exp2((S - row_max_safe[:, None]) * scale_log2)
         row_sum = row_sum * acc_scale + P.sum(axis=1)
@@ -92,7 +107,8 @@ def fa4_forward(q, k, v, scale: float, causal: bool = False, block_n: int = 128,
     out[nz] = O[nz] / row_sum[nz, None]
     lse = np.full(Nq, -np.inf)
     lse[nz] = np.log(row_sum[nz]) + row_max[nz] * float(scale)
-    return dict(o=out, lse=lse, rescales=rescales, trace=states)
+    return dict(o=out, lse=lse, rescales=rescales, rescale_rows=rescale_rows,
+                near_ties=near_ties, trace=states)
 
 
 def update_row(row_max: float, row_sum: float, O, S, V, scale_log2: float,

@@ -34,6 +34,13 @@ def test_version_and_defaults():
     assert fa.fa_version() >= 100
     o = fa.fa_fwd_opts_default()
     assert (o.o_dtype, o.rescale_threshold, o.schedule, o.kv_heads) == (0, 8.0, 0, 0)
+    assert o.rescale_counts is None   # NULL: no counting
+
+
+def test_rescale_counts_pointer():
+    assert check(opts=opts(rescale_counts=P)) == fa.FA_OK
+    assert check(opts=opts(rescale_counts=P + 2)) == fa.FA_ERR_INVALID_ARG   # 4-byte aligned
+    assert check(opts=opts(rescale_counts=P + 4)) == fa.FA_OK
 
 
 def test_status_strings():

@@ -135,3 +135,29 @@ def test_fully_masked_first_blocks_stay_finite():
     assert np.all(np.isfinite(r["o"])) and np.all(np.isfinite(r["lse"]))
     o, lse = oracle.attention(q[None, :, None], k[None, :, None], v[None, :, None], 0.5, True)
     np.testing.assert_allclose(r["o"], o[0, :, 0], atol=1e-12)
+
+
+def test_rescale_counts_per_row_by_hand():
+    """Per-row reference moves, one key per block, scale ln 2 (scale * log2 e is exactly
+    1.0 in fp64, so delta is the score gap).  Scores of row 0: 0, 5, 9, 12, 30, 31; row 1
+    (twice the query): 0, 10, 18, 24, 60, 62.  Always rescale (tau 0): every new running
+    maximum after the first key moves the reference -- 5 per row.  tau 8: row 0 moves at
+    9 (gap 9) and 30 (gap 21): 2; row 1 at 10, 24 (gap 14 over 10; 18 is only 8 above 10:
+    delta = -8 keeps the reference) and 60: 3 -- the tie at exactly -8 is a near tie."""
+    a = np.array([0.0, 5.0, 9.0, 12.0, 30.0, 31.0])
+    q = np.array([[1.0], [2.0]])
+    k = a[:, None]
+    v = np.eye(6)
+    scale = math.log(2.0)
+    r0 = model.fa4_forward(q, k, v, scale, block_n=1, threshold=0.0)
+    assert list(r0["rescale_rows"]) == [5, 5] and r0["rescales"] == 10
+    r8 = model.fa4_forward(q, k, v, scale, block_n=1, threshold=8.0)
+    assert list(r8["rescale_rows"]) == [2, 3] and r8["rescales"] == 5
+    assert list(r8["near_ties"]) == [0, 1]
+    # the per-row counts add up to the total on a random causal problem
+    rng = np.random.default_rng(9)
+    qq, kk, vv = (rng.standard_normal((100, 8)) for _ in range(3))
+    kk[rng.choice(100, 3, replace=False)] *= 8.0
+    for tau in (0.0, 8.0):
+        r = model.fa4_forward(qq, kk, vv, 0.5, causal=True, block_n=16, threshold=tau)
+        assert int(r["rescale_rows"].sum()) == r["rescales"]
