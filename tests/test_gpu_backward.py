@@ -98,6 +98,10 @@ def test_bwd_varlen():
     w = wl.make_varlen(2, 128, seed=75, lengths=[77, 256], causal=False)
     do = wl.make_dout(w, seed=76)
     print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "varlen d128 full"))
+    # sequences of length 0 inside the batch
+    w = wl.make_varlen(2, 128, seed=77, lengths=[5, 0, 130, 0, 64], causal=True)
+    do = wl.make_dout(w, seed=78)
+    print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "varlen with empty sequences"))
 
 
 def test_bwd_mid_size():

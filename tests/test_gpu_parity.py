@@ -126,6 +126,14 @@ def test_small_varlen_full():
     _full_check(wnc, 8.0)
 
 
+def test_varlen_zero_length_sequences():
+    """Sequences of length 0 inside a packed batch own no rows and no tiles."""
+    w = wl.make_varlen(2, 128, seed=34, lengths=[5, 0, 130, 0, 64], causal=True)
+    _full_check(w, 8.0)
+    w64 = wl.make_varlen(3, 64, seed=35, lengths=[0, 257, 0], causal=False)
+    _full_check(w64, 0.0, o_dtype=1)
+
+
 def test_varlen_equals_separate_calls():
     """A packed call gives, bit for bit, what fixed-length calls on each sequence give."""
     w = wl.make_varlen(4, 128, seed=41, lengths=[513, 70, 256, 1000], causal=True)
