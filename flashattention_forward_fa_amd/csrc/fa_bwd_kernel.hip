@@ -108,10 +108,49 @@ struct BwdTile {
 // masking the heaviest tiles start first (longest-processing-time order): the
 // dQ tile m visits m + 1 key tiles' worth of blocks (reverse = true walks m
 // from the top), the dK/dV tile m visits the query blocks from m to the end
-// (reverse = false).  For packed sequences of unequal length the order is by
-// position only.
+// (reverse = false).  Packed sequences with a head count that is a multiple of
+// 8 use the XCD-aware order below; otherwise the order is by position only.
 __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads, int len_max,
                                            bool reverse, BwdTile &c) {
+    if (p.offsets && heads % kNumXcd == 0) {
+        // Varlen: workgroup t runs on XCD t % 8, which owns heads
+        // [x*HX, (x+1)*HX) of every sequence; on an XCD the tiles go sequence
+        // by sequence, head by head, each head's tiles longest first, so the
+        // tiles that read one head's K/V (or Q/dO) run together and share the
+        // XCD's L2.
+        const int lane = threadIdx.x & 63;
+        const int32_t *off = p.offsets;
+        const int x = t % kNumXcd, HX = heads / kNumXcd;
+        const int u = t / kNumXcd;
+        int base = 0;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int bb = b0 + lane;
+            const int nblk = bb < p.B ? (off[bb + 1] - off[bb] + kBwdRows - 1) / kBwdRows : 0;
+            const int v = nblk * HX;
+            int incl = v;
+#pragma unroll
+            for (int s = 1; s < 64; s <<= 1) {
+                const int o = __shfl_up(incl, s, 64);
+                if (lane >= s) incl += o;
+            }
+            const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+            if (u < base + total) {
+                const unsigned long long past = __ballot(base + incl > u);
+                const int lb = __ffsll((long long)past) - 1;
+                const int first = base + __builtin_amdgcn_readfirstlane(__shfl(incl - v, lb, 64));
+                const int n = __builtin_amdgcn_readfirstlane(__shfl(nblk, lb, 64));
+                const int r = u - first;
+                c.b = b0 + lb;
+                c.h = x * HX + r / n;
+                c.m = reverse ? n - 1 - r % n : r % n;
+                c.tok0 = off[c.b];
+                c.L_q = c.L_k = off[c.b + 1] - c.tok0;
+                return true;
+            }
+            base += total;
+        }
+        return false;
+    }
     const int nm = (len_max + kBwdRows - 1) / kBwdRows;
     const int nbh = p.B * heads;
     c.m = t / nbh;

@@ -125,15 +125,49 @@ __device__ __forceinline__ bool decode_fixed(int t, const FwdParams &p, TileCoor
     return true;
 }
 
-// Varlen, longest first: all tiles with query-tile index m = num_m-1 come
-// first (every sequence long enough, in sequence order, heads innermost), then
-// m = num_m-2, ...  Computed per wave from the offsets, with no host sync.
+// Varlen, longest first.  With H a multiple of 8, XCD-aware (below); else all
+// tiles with query-tile index m = num_m-1 come first (every sequence long
+// enough, in sequence order, heads innermost), then m = num_m-2, ...
+// Computed per wave from the offsets, with no host sync.
 template <int BM>
 __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoord &c) {
     const int lane = threadIdx.x & 63;
     const int32_t *off = p.offsets;
     int b = -1, m = -1, h = 0;
-    if (p.lpt) {
+    if (p.lpt && p.H % kNumXcd == 0) {
+        // Workgroup t runs on XCD t % 8, which owns query heads [x*HX, (x+1)*HX)
+        // of every sequence (an eighth of the work for any lengths).  On an
+        // XCD the tiles go sequence by sequence, head by head, each head's
+        // tiles longest first, so the tiles that read one head's K/V run
+        // together and share the XCD's L2.
+        const int x = t % kNumXcd, HX = p.H / kNumXcd;
+        const int u = t / kNumXcd;
+        int base = 0;
+        for (int b0 = 0; b0 < p.B && b < 0; b0 += 64) {
+            const int bb = b0 + lane;
+            const int nblk = bb < p.B ? (off[bb + 1] - off[bb] + BM - 1) / BM : 0;
+            const int v = nblk * HX;
+            int incl = v;     // inclusive prefix sum over the lanes
+#pragma unroll
+            for (int s = 1; s < 64; s <<= 1) {
+                const int o = __shfl_up(incl, s, 64);
+                if (lane >= s) incl += o;
+            }
+            const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+            if (u < base + total) {
+                const unsigned long long past = __ballot(base + incl > u);
+                const int lb = __ffsll((long long)past) - 1;
+                const int first = base + __builtin_amdgcn_readfirstlane(__shfl(incl - v, lb, 64));
+                const int n = __builtin_amdgcn_readfirstlane(__shfl(nblk, lb, 64));
+                const int r = u - first;
+                b = b0 + lb;
+                h = x * HX + r / n;
+                m = n - 1 - r % n;
+            }
+            base += total;
+        }
+        if (b < 0) return false;
+    } else if (p.lpt) {
         int rem = t;
         for (int lvl = p.num_m - 1; lvl >= 0 && b < 0; --lvl) {
             int cnt = 0;

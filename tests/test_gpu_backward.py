@@ -104,6 +104,67 @@ def test_bwd_varlen():
     print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "varlen with empty sequences"))
 
 
+def row_term_allowance(q, k, v, do, scale, causal):
+    """Four-sigma allowances for the D_i row term (derivation in
+    test_bwd_full_size_sampled) on every row of one (sequence, K/V head) slice:
+    q, do [Nq, G, d]; k, v [Nk, d].  Returns (dQ allowance [Nq, G, d], dK
+    allowance [Nk, d])."""
+    Nq, G, d = q.shape
+    Nk = k.shape[0]
+    o, lse = oracle.attention(q[None], k[None, :, None], v[None, :, None], scale, causal)
+    kbar, _ = oracle.attention(q[None], k[None, :, None], k[None, :, None], scale, causal)
+    sig = np.sqrt(np.sum((do * (2.0 ** -9 * np.abs(o[0]) + 3e-4)) ** 2, axis=2))     # [Nq, G]
+    allow_q = abs(scale) * 4.0 * sig[:, :, None] * np.abs(kbar[0])
+    sc = scale * np.einsum("igc,jc->igj", q, k)
+    seen = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        seen = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)
+    lse_t = lse[0].T[:, :, None]
+    pr = np.where(seen[:, None, :], np.exp(np.where(seen[:, None, :], sc - lse_t, -np.inf)), 0.0)
+    allow_k = 4.0 * abs(scale) * np.sqrt(np.einsum("igj,igc->jc", (pr * sig[:, :, None]) ** 2, q ** 2))
+    return allow_q, allow_k
+
+
+def varlen_allowances(w, dout_bits):
+    """row_term_allowance over every sequence and K/V head of a packed workload:
+    ([T, H, d], [T, Hkv, d])."""
+    q, k, v = parity.inputs_f64(w)
+    do = wl.bf16_to_f64(dout_bits)
+    G = w.H // w.kv_heads
+    aq = np.zeros(q.shape)
+    ak = np.zeros(k.shape)
+    for b in range(len(w.lengths)):
+        t = slice(int(w.offsets[b]), int(w.offsets[b + 1]))
+        if t.stop == t.start:
+            continue
+        for kvh in range(w.kv_heads):
+            hs = slice(kvh * G, (kvh + 1) * G)
+            aq[t, hs], ak[t, kvh] = row_term_allowance(q[t, hs], k[t, kvh], v[t, kvh], do[t, hs],
+                                                       w.scale, w.causal)
+    return aq, ak
+
+
+def test_bwd_varlen_xcd_order():
+    """Head counts that are a multiple of 8 take the XCD-aware varlen order in both
+    kernels: more than 64 sequences (two scan rounds) with empty ones; 16 query
+    heads over 8 K/V heads.  Most rows here are short causal rows, where one key
+    can dominate, so dQ and dK carry the D_i row-term allowance of the full-size
+    checks."""
+    lengths = [int(x) for x in np.random.default_rng(79).integers(0, 200, 70)]
+    lengths[3] = lengths[64] = 0
+    lengths[65] = 1
+    w = wl.make_varlen(8, 64, seed=79, lengths=lengths, causal=True)
+    do = wl.make_dout(w, seed=80)
+    aq, ak = varlen_allowances(w, do)
+    print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "varlen 70 sequences H8",
+                        extra=(aq, ak, 0.0)))
+    w = wl.make_varlen(16, 128, seed=81, lengths=[300, 0, 129, 513, 64], causal=True, Hkv=8)
+    do = wl.make_dout(w, seed=82)
+    aq, ak = varlen_allowances(w, do)
+    print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "varlen H16 over 8 K/V heads",
+                        extra=(aq, ak, 0.0)))
+
+
 def test_bwd_mid_size():
     """Many key and query blocks: B=1, H=4, N=1024, d=128, causal."""
     w = wl.make_fixed(1, 4, 1024, 1024, 128, seed=77, causal=True)

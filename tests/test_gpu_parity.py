@@ -134,6 +134,25 @@ def test_varlen_zero_length_sequences():
     _full_check(w64, 0.0, o_dtype=1)
 
 
+def _xcd_order_lengths(seed):
+    """70 sequence lengths in [0, 200) with two empty sequences and one of length 1:
+    more than 64 sequences, so the per-wave scan over the offsets takes two rounds."""
+    lengths = [int(x) for x in np.random.default_rng(seed).integers(0, 200, 70)]
+    lengths[3] = lengths[64] = 0
+    lengths[65] = 1
+    return lengths
+
+
+def test_varlen_xcd_order():
+    """Head counts that are a multiple of 8 take the XCD-aware longest-first order
+    (each XCD owns an eighth of the heads of every sequence, tiles of one head
+    together): many and empty sequences, d = 64 and 128, grouped K/V heads."""
+    w = wl.make_varlen(8, 64, seed=36, lengths=_xcd_order_lengths(36), causal=True)
+    _full_check(w, 8.0)
+    w128 = wl.make_varlen(16, 128, seed=37, lengths=[300, 0, 129, 513, 64], causal=True, Hkv=8)
+    _full_check(w128, 8.0)
+
+
 def test_varlen_equals_separate_calls():
     """A packed call gives, bit for bit, what fixed-length calls on each sequence give."""
     w = wl.make_varlen(4, 128, seed=41, lengths=[513, 70, 256, 1000], causal=True)
