@@ -158,7 +158,9 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
     p.Nk = Nk;
     p.num_m = (Nq + fa::fwd_block_m(d) - 1) / fa::fwd_block_m(d);
     p.num_tiles = B * H * p.num_m;
-    const bool lpt_default = causal != 0;
+    // Tiles of unequal work (causal rows, sequences of different lengths) run
+    // longest first; with packed sequences that order is also the XCD-aware one.
+    const bool lpt_default = causal != 0 || varlen_offsets != nullptr;
     p.lpt = op.schedule == FA_SCHEDULE_LPT ? 1 : op.schedule == FA_SCHEDULE_LINEAR ? 0 : lpt_default;
     // The kernel tracks the maximum of the unscaled scores, which is the
     // maximum of the scaled ones only for scale > 0.  A negative scale is

@@ -179,6 +179,15 @@ def test_schedules_agree_bitwise():
     ref = parity.run_gpu(wv, schedule=2, tensors=tv)
     got = parity.run_gpu(wv, schedule=1, tensors=tv)
     assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+    # 8 heads: the longest-first order of packed sequences is the XCD-aware one,
+    # and it is the default for packed sequences with or without causal masking
+    for causal in (False, True):
+        wx = wl.make_varlen(8, 128, seed=6, lengths=[700, 0, 129, 64, 300], causal=causal)
+        tx = parity.to_device(wx)
+        ref = parity.run_gpu(wx, schedule=1, tensors=tx)
+        for sch in (0, 2):
+            got = parity.run_gpu(wx, schedule=sch, tensors=tx)
+            assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (causal, sch)
 
 
 def test_outputs_stay_in_bounds():
