@@ -34,7 +34,7 @@ def test_worked_example_rounds_always_rescale():
 
 
 def test_worked_example_rounds_conditional():
-    """Threshold 8: in round 2 delta = (1 - 2) * 1 = -1 >= -8, so the reference stays 1.
+    """Threshold 8: at the example's second K/V block delta = (1 - 2) * 1 = -1 >= -8, so the reference stays 1.
 
     Derived from the update rule: P^(2) = 2^(S - 1) = [[2, 1/2], [1, 2]],
     l = 3/2 + (5/2, 3) = (4, 9/2), O = O^(1) + P^(2) V_2 = [[7/2, 3], [6, 3/2]];
