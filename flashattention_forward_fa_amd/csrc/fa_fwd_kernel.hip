@@ -17,15 +17,17 @@
 //
 // and finally O = o / l (0 when l = 0) and LSE = ln l + r * scale ("Flash
 // Attention 4", section "rescale and write-back": valid for any consistent
-// reference).  O is normalised by the row sum of the bf16-rounded P that the
-// PV product used, LSE by the fp32 row sum (see the softmax step).  The first block of a row starts from r = -inf, so delta = -inf
+// reference).  The first block of a row starts from r = -inf, so delta = -inf
 // switches to the candidate with alpha = 0 on a zero state, which is the
 // page's first-block case (taken without evaluating delta, which would be
 // -inf * 0 for scale 0).  A candidate of -inf (every key so far masked) keeps
-// r = -inf with alpha = 1.  The row sum adds the same bf16-rounded P that the
-// PV product uses (the pages sum P before rounding it): with a stale
-// reference the dominant weight is 2^x rather than exactly 1, and summing the
-// rounded values keeps O a convex combination of the V rows.
+// r = -inf with alpha = 1.
+//
+// Two row sums: O is normalised by the sum of the same bf16-rounded P that the
+// PV product uses (the pages sum P before rounding it: with a stale reference
+// the dominant weight is 2^x rather than exactly 1, and summing the rounded
+// values keeps O a convex combination of the V rows), LSE by the fp32 sum of
+// the unrounded P.
 //
 // Mapping onto CDNA4 (this is not the pages' Blackwell/Hopper/Ampere design):
 //
@@ -56,8 +58,10 @@
 //   the 16-byte K reads and the transpose reads meet no bank conflict.
 // * Tiles are mapped XCD-aware: workgroups are dispatched round-robin over the
 //   8 XCDs, so XCD x is given a contiguous set of (batch, head) pairs and its
-//   L2 holds their K/V.  Causal and varlen tiles go longest first (LPT,
-//   "FlashAttention-4 (下)", section 6).
+//   L2 holds their K/V.  Causal tiles go longest first (LPT, "FlashAttention-4
+//   (下)", section 6).  Packed sequences give XCD x an eighth of the heads of
+//   every sequence and run each head's tiles together, longest first, so that
+//   the tiles reading one head's K/V share the L2 (decode_varlen).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
