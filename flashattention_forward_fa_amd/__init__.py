@@ -10,7 +10,9 @@ Entry points mirror ``include/fa.h``: ``fa_fwd``, ``fa_fwd_ex``,
 ``fa_version``.  Pointer arguments accept torch tensors (their data pointer) or
 integers; ``stream`` accepts a ``torch.cuda.Stream``, an integer hipStream_t or
 None (torch's current stream).  ``attention`` is a convenience wrapper that
-allocates O and LSE with torch and raises on a non-zero status.
+allocates O and LSE with torch and raises on a non-zero status; ``attention_bwd``
+does the same for the backward, and ``flash_attention`` joins the two as one
+differentiable torch operation.
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
            "FA_DTYPE_BF16", "FA_DTYPE_F32", "FA_SCHEDULE_AUTO", "FA_SCHEDULE_LINEAR",
            "FA_SCHEDULE_LPT", "FaFwdOpts", "FaError", "library_path", "load", "fa_fwd",
            "fa_fwd_ex", "fa_fwd_check", "fa_status_string", "fa_fwd_opts_default",
-           "fa_version", "attention"]
+           "fa_version", "fa_bwd", "fa_bwd_check", "fa_bwd_workspace_size", "attention",
+           "attention_bwd", "flash_attention"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
 FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
@@ -235,3 +238,44 @@ def attention_bwd(q, k, v, o, lse, dout, scale: float, causal: bool, *, varlen_o
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+_function = None
+
+
+def _flash_attention_function():
+    """The torch.autograd.Function behind flash_attention (built on first use,
+    so that importing this module does not import torch)."""
+    global _function
+    if _function is None:
+        import torch
+
+        class FlashAttentionFunction(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, causal, varlen_offsets, max_seqlen, rescale_threshold):
+                o, lse = attention(q, k, v, scale, causal, varlen_offsets=varlen_offsets,
+                                   max_seqlen=max_seqlen, rescale_threshold=rescale_threshold)
+                extra = (varlen_offsets,) if varlen_offsets is not None else ()
+                ctx.save_for_backward(q, k, v, o, lse, *extra)
+                ctx.scale, ctx.causal, ctx.max_seqlen = scale, causal, max_seqlen
+                return o
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, o, lse, *extra = ctx.saved_tensors
+                dq, dk, dv = attention_bwd(q, k, v, o, lse, dout.contiguous(), ctx.scale,
+                                           ctx.causal, varlen_offsets=extra[0] if extra else None,
+                                           max_seqlen=ctx.max_seqlen)
+                return dq, dk, dv, None, None, None, None, None
+
+        _function = FlashAttentionFunction
+    return _function
+
+
+def flash_attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_seqlen=None,
+                    rescale_threshold: float = 8.0):
+    """O = softmax(scale Q K^T) V as a differentiable torch operation: the forward
+    runs fa_fwd_ex (bf16 O; LSE kept for the backward), the backward fa_bwd on
+    the saved O and LSE.  Shapes as for attention(); returns o."""
+    return _flash_attention_function().apply(q, k, v, scale, causal, varlen_offsets, max_seqlen,
+                                             rescale_threshold)
