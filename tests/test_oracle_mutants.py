@@ -1,8 +1,8 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU) and check that
 the pins catch every one of them.  This shows the pins constrain each part of
 the oracle: the scale, the maximum subtraction, the normaliser, the key/value
-strides, the K/V head of each query head, the mask alignment, the LSE and the
-backward's terms."""
+strides, the K/V head of each query head, the mask alignment, the LSE, the
+backward's terms, and the packed-sequence and sampled-row entry points."""
 import os
 import subprocess
 
@@ -40,6 +40,21 @@ MUTANTS = {
     "bwd_rows_dk_from_dout": ("ok[c] += scale * ds * qi[c];", "ok[c] += scale * ds * doi[c];"),
     "bwd_rows_row_term_unweighted": ("D += exp(s_buf[j] - L) * dot;", "D += dot;"),
     "lse_wrong_slot": ("lse + (b * H + h) * Nq + i);", "lse + (h * B + b) * Nq + i);"),
+    # packed sequences and the sampled-rows entry point
+    "varlen_lse_token_major": ("lse + h * T + t);", "lse + t * H + h);"),
+    "varlen_keys_from_token_zero": ("attention_row(q + (t * H + h) * d, k + (start * Hkv + h / group) * d,",
+                                    "attention_row(q + (t * H + h) * d, k + (h / group) * d,"),
+    "rows_packed_query_ignores_start": ("qi = q + ((start + i) * H + h) * d;", "qi = q + (i * H + h) * d;"),
+    "rows_fixed_batch_dropped": ("                    qi = q + ((b * Nq + i) * H + h) * d;\n"
+                                 "                    kb = k + (b * Nk * Hkv + h / group) * d;",
+                                 "                    qi = q + (i * H + h) * d;\n"
+                                 "                    kb = k + (b * Nk * Hkv + h / group) * d;"),
+    "rows_alignment_from_nk": ("                    vb = v + (b * Nk * Hkv + h / group) * d;\n"
+                               "                    nvalid = valid_keys(i, Nq, Nk, causal);",
+                               "                    vb = v + (b * Nk * Hkv + h / group) * d;\n"
+                               "                    nvalid = valid_keys(i, Nk, Nk, causal);"),
+    "bwd_varlen_keys_from_token_zero": ("bwd_head(q + (start * H + h) * d, k + (start * Hkv + kvh) * d,",
+                                        "bwd_head(q + (start * H + h) * d, k + (kvh) * d,"),
 }
 
 
