@@ -151,9 +151,15 @@ def test_rescale_counts_per_row_by_hand():
     scale = math.log(2.0)
     r0 = model.fa4_forward(q, k, v, scale, block_n=1, threshold=0.0)
     assert list(r0["rescale_rows"]) == [5, 5] and r0["rescales"] == 10
-    r8 = model.fa4_forward(q, k, v, scale, block_n=1, threshold=8.0)
+    r8 = model.fa4_forward(q, k, v, scale, block_n=1, threshold=8.0, trace=True)
     assert list(r8["rescale_rows"]) == [2, 3] and r8["rescales"] == 5
     assert list(r8["near_ties"]) == [0, 1]
+    # which blocks move, not only how many: the reference after each block, by hand
+    # (row 1 keeps 10 at 18, where delta is exactly -8; a strict test would move there
+    # and still count 3 moves: 10, 18, 60)
+    refs = np.array([st["row_max"] for st in r8["trace"]])
+    assert refs[:, 0].tolist() == [0.0, 0.0, 9.0, 9.0, 30.0, 30.0]
+    assert refs[:, 1].tolist() == [0.0, 10.0, 10.0, 24.0, 60.0, 60.0]
     # the per-row counts add up to the total on a random causal problem
     rng = np.random.default_rng(9)
     qq, kk, vv = (rng.standard_normal((100, 8)) for _ in range(3))
