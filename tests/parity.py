@@ -111,8 +111,9 @@ def sample_rows(w, n_random: int, seed: int = 0):
             for i in sorted({0, 1, 2, 31, 32, 63, 64, 255, 256, L // 2, L - 2, L - 1}):
                 if 0 <= i < L:
                     rows.append((b, int(rng.integers(w.H)), i))
-        for _ in range(n_random):
-            b = int(rng.integers(len(w.lengths)))
+        live = [b for b, L in enumerate(w.lengths) if int(L) > 0]   # empty sequences own no rows
+        for _ in range(n_random if live else 0):
+            b = live[int(rng.integers(len(live)))]
             rows.append((b, int(rng.integers(w.H)), int(rng.integers(int(w.lengths[b])))))
     else:
         edges = sorted({0, 1, 2, 31, 32, 63, 64, 127, 128, 255, 256, 257, w.Nq // 2,
