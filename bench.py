@@ -59,7 +59,8 @@ def traffic_from_profile(workload: str):
     path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}.pmc.txt")
     if not os.path.exists(path):
         return None
-    text = open(path).read()
+    with open(path) as f:
+        text = f.read()
     fields = dict(re.findall(r"^([a-z0-9_]+):\s*(\S+)\s*$", text, flags=re.M))
     if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None

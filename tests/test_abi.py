@@ -10,12 +10,18 @@ import pytest
 
 import flashattention_forward_fa_amd as fa
 
+
+def _read(path):
+    with open(path) as f:
+        return f.read()
+
+
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
 P = 1 << 20          # a 16-byte aligned stand-in address; the checks never dereference it
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = _read(HEADER)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
 

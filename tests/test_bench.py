@@ -2,6 +2,7 @@
 lookup's source-hash check, and the oracle baseline record."""
 import json
 import os
+import pathlib
 import subprocess
 import sys
 
@@ -28,7 +29,7 @@ def test_traffic_needs_the_current_kernel_source(tmp_path, monkeypatch):
     for rel in bench.KERNEL_SOURCES:   # the hash reads the sources under ROOT
         dst = tmp_path / rel
         dst.parent.mkdir(parents=True, exist_ok=True)
-        dst.write_bytes(open(os.path.join(ROOT, rel), "rb").read())
+        dst.write_bytes(pathlib.Path(ROOT, rel).read_bytes())
     h = bench.kernel_source_hash()
     (prof / "fa_fwd_w.pmc.txt").write_text(
         f"header\nkernel_source_sha256_16: {h}\nhbm_bytes_per_launch: 12345\n")

@@ -11,6 +11,12 @@ import pytest
 from oracle import model as _model
 from tests import test_model as pins
 
+
+def _read(path):
+    with open(path) as f:
+        return f.read()
+
+
 SRC = _model.__file__
 
 MUTANTS = {
@@ -65,15 +71,16 @@ def _load(text, name):
 
 
 def test_unmutated_copy_passes(monkeypatch):
-    monkeypatch.setattr(pins, "model", _load(open(SRC).read(), "model_copy"))
+    monkeypatch.setattr(pins, "model", _load(_read(SRC), "model_copy"))
     for check in _checks():
         check()
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")   # mutants may produce inf * 0
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_model_mutant_is_caught(name, monkeypatch):
     old, new = MUTANTS[name]
-    src = open(SRC).read()
+    src = _read(SRC)
     assert src.count(old) == 1, f"mutation site for {name} not unique"
     monkeypatch.setattr(pins, "model", _load(src.replace(old, new), f"model_{name}"))
     caught = 0

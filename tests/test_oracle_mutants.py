@@ -11,6 +11,12 @@ import pytest
 import oracle
 from tests import oracle_pins
 
+
+def _read(path):
+    with open(path) as f:
+        return f.read()
+
+
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTANTS = {
@@ -68,10 +74,11 @@ def _run_pins(orc):
     return failed
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")   # mutants may produce NaN or inf
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, tmp_path):
     old, new = MUTANTS[name]
-    src = open(SRC).read()
+    src = _read(SRC)
     assert src.count(old) == 1, f"mutation site for {name} not unique"
     path = tmp_path / f"oracle_{name}.c"
     path.write_text(src.replace(old, new))
