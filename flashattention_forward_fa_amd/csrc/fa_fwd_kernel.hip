@@ -193,7 +193,7 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
                     const int n = __popcll(mask);
                     if (target < n) {
                         const unsigned long long below = lane ? (mask & ((1ull << lane) - 1ull)) : 0ull;
-                        const bool hit = ((mask >> lane) & 1ull) && __popcll(below) == target;
+                        const bool hit = ((mask >> lane) & 1ull) && (int)__popcll(below) == target;
                         const unsigned long long hm = __ballot(hit);
                         b = b0 + __ffsll((long long)hm) - 1;
                         m = lvl;
