@@ -165,6 +165,16 @@ def test_bwd_varlen_xcd_order():
                         extra=(aq, ak, 0.0)))
 
 
+def test_bwd_varlen_many_short_sequences():
+    """1000 sequences of 0 to 20 tokens with 8 heads (16 scan rounds in both kernels)."""
+    lengths = [int(x) for x in np.random.default_rng(83).integers(0, 21, 1000)]
+    w = wl.make_varlen(8, 64, seed=83, lengths=lengths, causal=True)
+    do = wl.make_dout(w, seed=84)
+    aq, ak = varlen_allowances(w, do)
+    print(compare_grads(run_bwd(w, do), ref_bwd(w, do), "1000 short sequences H8",
+                        extra=(aq, ak, 0.0)))
+
+
 def test_bwd_mid_size():
     """Many key and query blocks: B=1, H=4, N=1024, d=128, causal."""
     w = wl.make_fixed(1, 4, 1024, 1024, 128, seed=77, causal=True)

@@ -153,6 +153,16 @@ def test_varlen_xcd_order():
     _full_check(w128, 8.0)
 
 
+def test_varlen_many_short_sequences():
+    """1000 sequences of 0 to 20 tokens (about 5% empty) with 8 heads: the XCD-aware
+    order's scan over the offsets takes 16 rounds of 64 sequences."""
+    lengths = [int(x) for x in np.random.default_rng(38).integers(0, 21, 1000)]
+    w = wl.make_varlen(8, 64, seed=38, lengths=lengths, causal=True)
+    _full_check(w, 8.0)
+    wnc = wl.make_varlen(8, 128, seed=39, lengths=lengths[:300], causal=False)
+    _full_check(wnc, 0.0)
+
+
 def test_varlen_equals_separate_calls():
     """A packed call gives, bit for bit, what fixed-length calls on each sequence give."""
     w = wl.make_varlen(4, 128, seed=41, lengths=[513, 70, 256, 1000], causal=True)
