@@ -7,11 +7,20 @@ runs in one kernel launch on inputs already resident in HBM.  The default
 workload is causal attention, B=2, H=32, Nq=Nk=4096, d=128, bf16 in, bf16 O,
 fp32 LSE, scale 1/sqrt(128), seeded N(0,1) inputs.
 
+Timing: first a settle phase of back-to-back launches until --settle-ms of
+wall time have passed (the shader clock of a cold GPU takes a few hundred
+milliseconds of load to reach its steady value, whatever --warmup says), then
+--warmup untimed steps, then exactly --steps timed steps between two
+synchronisations.  While those run, a one-wavefront probe on a second stream
+samples the shader clock against the constant-rate clock (fa_clock_probe), so
+the line states the clock the throughput was measured at.
+
 Prints one JSON line:
   value        TFLOP/s = 4*B*H*Nq*Nk*d/2 (causal) / ms_per_step
   roofline     the kernel's achieved TFLOP/s from per-launch HIP events on the
                launch stream (a second loop of K launches), against the bf16
-               dense MFMA peak (2.5 PFLOP/s);
+               dense MFMA peak (2.5 PFLOP/s, nominal at 2.4 GHz), and against
+               CUs x 4096 flop/clk x the measured shader clock (peak_at_sclk);
                traffic = HBM bytes per launch from the committed rocprofv3
                FETCH_SIZE / WRITE_SIZE summary (null unless it was taken on the
                kernel source as it is now)
@@ -38,7 +47,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA (256 CUs at 2.4 GHz)
+MFMA_BF16_FLOP_PER_CLK_CU = 4096  # dense bf16 matrix-core flops per clock per CU
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_forward_fa_amd/csrc/fa_fwd_kernel.hip",
                   "flashattention_forward_fa_amd/csrc/fa_device.h",
@@ -136,8 +146,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps first; the clocks take a few hundred launches to settle")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps after the settle phase")
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="launch back to back for at least this long before the warm-up (clocks)")
     ap.add_argument("--config", type=int, default=3, help="workload 1-5 (3 = the headline)")
     ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold")
     ap.add_argument("--backward", action="store_true",
@@ -218,18 +229,43 @@ def main():
             if st != fa.FA_OK:
                 raise fa.FaError(st)
 
+    # Settle: back-to-back launches until settle_ms of wall time have passed.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    settle_launches = 0
+    while True:
+        for _ in range(10):
+            step()
+        settle_launches += 10
+        torch.cuda.synchronize()
+        settle_ms = (time.perf_counter() - t0) * 1e3
+        if settle_ms >= args.settle_ms:
+            break
+    est_ms = settle_ms / settle_launches
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # The whole job: K steps back to back, wall clock between two syncs.
+    # The whole job: K steps back to back, wall clock between two syncs; the
+    # clock probe samples for about 90% of the expected duration beside them.
+    probe_interval_us = 10
+    n_probe = max(2, min(1000000, int(0.9 * est_ms * args.steps * 1e3 / probe_interval_us)))
+    samples = torch.zeros(2 * n_probe, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
     torch.cuda.synchronize()
+    st_probe, ref_hz = fa.fa_clock_probe(samples, n_probe, probe_interval_us, side)
+    if st_probe != fa.FA_OK:
+        raise fa.FaError(st_probe, "fa_clock_probe")
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    sm = samples.cpu().numpy().astype(np.float64).reshape(-1, 2)
+    sclk_ghz = float((sm[-1, 0] - sm[0, 0]) / (sm[-1, 1] - sm[0, 1]) * ref_hz / 1e9)
+    probe_ms = float((sm[-1, 1] - sm[0, 1]) / ref_hz * 1e3)
 
     # The kernel: K more launches, each bracketed by HIP events recorded on
     # the launch stream (the events add small gaps, so this loop is not the
@@ -249,6 +285,8 @@ def main():
     flops = w.flops() * (2.5 if args.backward else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    peak_at_sclk = cus * MFMA_BF16_FLOP_PER_CLK_CU * sclk_ghz * 1e9 / 1e12
     traffic = None if args.backward else traffic_from_profile(w.name)
     # The headline metric names its workload; another --config or --kv-heads names its own.
     metric = "attention fwd TFLOP/s and % of bf16 MFMA peak (d=128, N=4096 causal)"
@@ -264,6 +302,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": round(settle_ms, 1),
+        "settle_launches": settle_launches,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -276,6 +316,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
+                     "sclk_ghz": round(sclk_ghz, 4),
+                     "sclk_window_ms": round(probe_ms, 3),
+                     "peak_at_sclk": round(peak_at_sclk, 1),
+                     "frac_at_sclk": round(achieved / peak_at_sclk, 4),
+                     "cus": cus,
                      "avg_launch_ms": round(avg_launch_ms, 5),
                      "median_launch_ms": round(median_launch_ms, 5),
                      "min_launch_ms": round(sorted_ms[0], 5),

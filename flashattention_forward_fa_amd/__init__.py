@@ -23,7 +23,8 @@ __all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
            "FA_DTYPE_BF16", "FA_DTYPE_F32", "FA_SCHEDULE_AUTO", "FA_SCHEDULE_LINEAR",
            "FA_SCHEDULE_LPT", "FaFwdOpts", "FaError", "library_path", "load", "fa_fwd",
            "fa_fwd_ex", "fa_fwd_check", "fa_status_string", "fa_fwd_opts_default",
-           "fa_version", "fa_bwd", "fa_bwd_check", "fa_bwd_workspace_size", "attention",
+           "fa_version", "fa_bwd", "fa_bwd_check", "fa_bwd_workspace_size", "fa_clock_probe",
+           "attention",
            "attention_bwd", "flash_attention"]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
@@ -82,6 +83,8 @@ def load():
     lib.fa_bwd_check.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int64
+    lib.fa_clock_probe.argtypes = [vp, i, i, ctypes.POINTER(ctypes.c_double), vp]
+    lib.fa_clock_probe.restype = i
     _lib = lib
     return lib
 
@@ -147,12 +150,42 @@ def fa_bwd_workspace_size(B: int, H: int, Nq: int) -> int:
     return int(load().fa_bwd_workspace_size(B, H, Nq))
 
 
+def fa_clock_probe(samples, n: int, interval_us: int, stream=None):
+    """Launch the shader-clock probe (diagnostics); returns (status, ref_hz).
+    samples: device buffer of 2*n uint64 (e.g. an int64 tensor)."""
+    ref = ctypes.c_double(0.0)
+    st = load().fa_clock_probe(_ptr(samples), int(n), int(interval_us), ctypes.byref(ref),
+                               _stream(stream))
+    return st, ref.value
+
+
 def fa_status_string(status: int) -> str:
     return load().fa_status_string(int(status)).decode()
 
 
 def fa_version() -> int:
     return load().fa_version()
+
+
+def _same_gpu(**tensors):
+    """Raise ValueError unless every given tensor (None entries skipped) lives on
+    one GPU: a host pointer handed to a kernel would be dereferenced on the
+    device.  Runs before the library is loaded or anything is launched."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"{name} must be a GPU tensor (got device {getattr(t, 'device', '?')})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+    if dev is not None:
+        import torch
+        if dev.index is not None and dev.index != torch.cuda.current_device():
+            raise ValueError(f"the tensors are on {dev}, the current device is "
+                             f"cuda:{torch.cuda.current_device()}: launches go to the current device")
 
 
 def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_seqlen=None,
@@ -166,8 +199,12 @@ def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_s
     Hkv (read from k's shape) divides H; query heads h*G .. h*G+G-1, G = H/Hkv,
     share K/V head h.  rescale_counts=True also returns each row's count of
     rescale events (int32, laid out like lse): (o, lse, counts).
+    q, k, v and the offsets must be on one GPU (ValueError otherwise).
+    max_seqlen must be at least every sequence's length: the tile grid is sized
+    from it, and rows of a longer sequence would be left unwritten.
     """
     import torch
+    _same_gpu(q=q, k=k, v=v, varlen_offsets=varlen_offsets)
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
         raise TypeError("q, k, v must be bfloat16")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
@@ -212,8 +249,11 @@ def attention_bwd(q, k, v, o, lse, dout, scale: float, causal: bool, *, varlen_o
     """Allocate dQ, dK, dV and the workspace with torch and run fa_bwd.
 
     Shapes and layouts as for attention(); o and lse are the forward's outputs
-    (o bf16) and dout is dO, shaped like o.  Returns (dq, dk, dv), bf16."""
+    (o bf16) and dout is dO, shaped like o.  Returns (dq, dk, dv), bf16.
+    Every tensor must be on one GPU (ValueError otherwise); max_seqlen must be
+    at least every sequence's length."""
     import torch
+    _same_gpu(q=q, k=k, v=v, o=o, lse=lse, dout=dout, varlen_offsets=varlen_offsets)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         if t.dtype != torch.bfloat16 or not t.is_contiguous():
             raise TypeError(f"{name} must be a contiguous bfloat16 tensor")
@@ -277,5 +317,6 @@ def flash_attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None,
     """O = softmax(scale Q K^T) V as a differentiable torch operation: the forward
     runs fa_fwd_ex (bf16 O; LSE kept for the backward), the backward fa_bwd on
     the saved O and LSE.  Shapes as for attention(); returns o."""
+    _same_gpu(q=q, k=k, v=v, varlen_offsets=varlen_offsets)
     return _flash_attention_function().apply(q, k, v, scale, causal, varlen_offsets, max_seqlen,
                                              rescale_threshold)

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 SOURCES = [os.path.join(CSRC, "fa_fwd_kernel.hip"), os.path.join(CSRC, "fa_bwd_kernel.hip"),
-           os.path.join(CSRC, "fa_api.cpp")]
+           os.path.join(CSRC, "fa_clock.hip"), os.path.join(CSRC, "fa_api.cpp")]
 ARCH = "gfx950"
 
 # -amdgpu-mfma-vgpr-form: MFMA results and accumulators in ordinary VGPRs.  The

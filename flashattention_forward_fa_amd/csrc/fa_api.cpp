@@ -65,6 +65,38 @@ int check_bwd(const void *q, const void *k, const void *v, const void *o, const 
     return FA_OK;
 }
 
+// Launch the backward with D in `dsum` (already checked arguments).
+int run_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+            const void *dout, void *dq, void *dk, void *dv, float *dsum,
+            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+            const int32_t *varlen_offsets, int kv_heads, void *stream) {
+    fa::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dsum = dsum;
+    p.offsets = varlen_offsets;
+    p.B = B;
+    p.H = H;
+    p.group = kv_heads > 0 ? H / kv_heads : 1;
+    p.Hkv = H / p.group;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.scale = scale;
+    // P = exp2(S * scale * log2 e - LSE * log2 e); scale_log2 computed in
+    // double and rounded once, with its sign (LSE is given, no maximum kept).
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
+    (void)hipGetLastError();
+    const int err = fa::launch_bwd(p, d, causal != 0, stream);
+    return err == 0 ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,31 +121,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, scale,
                              causal, varlen_offsets, kv_heads);
     if (st != FA_OK) return st;
-    fa::BwdParams p;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
-    p.dout = dout;
-    p.lse = lse;
-    p.dq = dq;
-    p.dk = dk;
-    p.dv = dv;
-    p.dsum = (float *)workspace;
-    p.offsets = varlen_offsets;
-    p.B = B;
-    p.H = H;
-    p.group = kv_heads > 0 ? H / kv_heads : 1;
-    p.Hkv = H / p.group;
-    p.Nq = Nq;
-    p.Nk = Nk;
-    p.scale = scale;
-    // P = exp2(S * scale * log2 e - LSE * log2 e); scale_log2 computed in
-    // double and rounded once, with its sign (LSE is given, no maximum kept).
-    p.scale_log2 = (float)((double)scale * 1.4426950408889634073599246810019);
-    (void)hipGetLastError();
-    const int err = fa::launch_bwd(p, d, causal != 0, stream);
-    return err == 0 ? FA_OK : FA_ERR_HIP;
+    return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, (float *)workspace, B, H, Nq, Nk, d, scale,
+                   causal, varlen_offsets, kv_heads, stream);
 }
 
 void fa_fwd_opts_default(fa_fwd_opts *opts) {
@@ -193,6 +202,23 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            const int32_t *varlen_offsets, void *stream) {
     return fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, varlen_offsets, stream,
                      nullptr);
+}
+
+int fa_clock_probe(uint64_t *samples, int n, int interval_us, double *ref_hz, void *stream) {
+    if (!samples || ((uintptr_t)samples & 7u) || n < 2 || n > 1000000 || interval_us < 1 ||
+        interval_us > 100000 || !ref_hz)
+        return FA_ERR_INVALID_ARG;
+    int khz = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        return FA_ERR_HIP;
+    *ref_hz = 1000.0 * khz;
+    const double ticks = 1e-3 * khz * interval_us;
+    if (ticks < 1.0 || ticks > 1e7) return FA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    const int err = fa::launch_clock_probe(samples, n, (unsigned)ticks, stream);
+    return err == 0 ? FA_OK : FA_ERR_HIP;
 }
 
 const char *fa_status_string(int status) {

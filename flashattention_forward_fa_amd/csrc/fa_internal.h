@@ -56,4 +56,8 @@ struct BwdParams {
 // Enqueue the backward kernels (row sums D, then dQ, then dK and dV).
 int launch_bwd(const BwdParams &p, int d, bool causal, void *stream);
 
+// Enqueue the clock probe: n pairs (shader clock, constant-rate clock),
+// interval_ticks of the constant-rate clock apart.
+int launch_clock_probe(uint64_t *samples, int n, unsigned interval_ticks, void *stream);
+
 }  // namespace fa

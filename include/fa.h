@@ -176,6 +176,23 @@ int fa_bwd_check(const void *q, const void *k, const void *v, const void *o, con
                  const void *workspace, int B, int H, int Nq, int Nk, int d, float scale,
                  int causal, const int32_t *varlen_offsets, int kv_heads);
 
+/*
+ * Diagnostics, no part of the attention computation: measure the compute-unit
+ * (shader) clock, against which matrix-core throughput is priced.  One
+ * wavefront is launched on `stream` and records n pairs of 64-bit counts,
+ * samples[2*i] = shader-clock cycles and samples[2*i+1] = ticks of the
+ * device's constant-rate clock, interval_us microseconds apart on the latter.
+ * The clock over a window is (shader delta) / (constant delta) * *ref_hz.
+ * Launch it on a second stream beside the work being measured; it sleeps
+ * between samples.
+ *   samples   : device memory of 2*n uint64, 8-byte aligned, caller-owned
+ *   n         : 2 .. 1000000;  interval_us: 1 .. 100000
+ *   ref_hz    : host pointer; receives the constant-rate clock's frequency
+ * Returns FA_ERR_INVALID_ARG for bad arguments (nothing launched), FA_ERR_HIP
+ * if the device query or the launch fails.
+ */
+int fa_clock_probe(uint64_t *samples, int n, int interval_us, double *ref_hz, void *stream);
+
 /* A static, NUL-terminated description of a status code. */
 const char *fa_status_string(int status);
 

@@ -2,14 +2,19 @@
 through the C ABI, and compare with the oracle at the stated tolerances.
 
 Tolerances (O compared widened to fp64 against the unrounded fp64 oracle):
-  * max |O - O_ref| <= 1e-2 and mean |O - O_ref| <= 1e-3.
-  * The 1e-2 bound applies to the arithmetic: fp32-output runs are held to
-    it directly.  A bf16-output element additionally carries the rounding of
-    the final cast, up to half a bf16 ulp of its value (2^-8 relative: 0.0078
-    for |O| in [2, 4), 0.0156 in [4, 8)), which alone can exceed 1e-2; so
-    bf16-output runs are held to 1e-2 + half_ulp_bf16(|O_ref|).
+  * max |O - O_ref| <= 1e-2 and mean |O - O_ref| <= 1e-3, for fp32 and for
+    bf16 output alike.
+  * One exception, counted and reported: a bf16 value with |O_ref| >= 4 is
+    rounded by up to half a bf16 ulp of its binade (2^-6 = 0.0156 in [4, 8)),
+    which alone exceeds 1e-2; such elements are held to
+    max(1e-2, half_ulp_bf16(O_ref) + 1e-3) instead.  Below 4 the half ulp is
+    at most 0.0078 and the plain bound applies.
   * LSE: |LSE - LSE_ref| <= 1e-3 * max(1, |LSE_ref|) (a relative bound with a
     floor, since short causal rows can have LSE near 0); -inf must match -inf.
+
+Every comparison made with a ``label`` is recorded in ``RECORDS`` (max-abs,
+mean-abs, elements over 1e-2, elements under the representability allowance,
+LSE errors); the test session prints them at its end.
 """
 from __future__ import annotations
 
@@ -22,6 +27,9 @@ from flashattention_forward_fa_amd import workloads as wl
 O_MAX_ABS = 1e-2
 O_MEAN_ABS = 1e-3
 LSE_REL = 1e-3
+BF16_ALLOWANCE_FROM = 4.0   # |O_ref| from which a bf16 element's half ulp exceeds the bar
+
+RECORDS: list = []          # (label, stats) of every labelled comparison, in order
 
 
 def to_device(w):
@@ -61,13 +69,19 @@ def half_ulp_bf16(x):
 
 
 def o_bound(o_ref, bf16_out: bool):
-    if not bf16_out:
-        return np.full(np.shape(o_ref), O_MAX_ABS)
-    return O_MAX_ABS + half_ulp_bf16(o_ref)
+    """Per-element bound on |O - O_ref|: 1e-2, except bf16 elements with
+    |O_ref| >= 4, which get max(1e-2, half_ulp_bf16(O_ref) + 1e-3)."""
+    bound = np.full(np.shape(o_ref), O_MAX_ABS)
+    if bf16_out:
+        big = np.abs(o_ref) >= BF16_ALLOWANCE_FROM
+        if big.any():
+            bound[big] = np.maximum(O_MAX_ABS, half_ulp_bf16(o_ref[big]) + 1e-3)
+    return bound
 
 
-def compare(o, lse, o_ref, lse_ref, *, bf16_out: bool, what: str = ""):
-    """Assert the tolerances; returns a dict of error statistics."""
+def compare(o, lse, o_ref, lse_ref, *, bf16_out: bool, what: str = "", label: str | None = None):
+    """Assert the tolerances; returns a dict of error statistics (recorded in
+    RECORDS under ``label`` when one is given, also when an assertion fails)."""
     o = np.asarray(o, dtype=np.float64)
     o_ref = np.asarray(o_ref, dtype=np.float64)
     assert o.shape == o_ref.shape, f"{what}: O shape {o.shape} vs {o_ref.shape}"
@@ -75,8 +89,12 @@ def compare(o, lse, o_ref, lse_ref, *, bf16_out: bool, what: str = ""):
     err = np.abs(o - o_ref)
     bound = o_bound(o_ref, bf16_out)
     bad = err > bound
-    stats = dict(o_max_abs=float(err.max(initial=0.0)), o_mean_abs=float(err.mean()) if err.size else 0.0,
-                 n_over_1e2=int(np.count_nonzero(err > O_MAX_ABS)))
+    stats = dict(n_elem=int(err.size), o_max_abs=float(err.max(initial=0.0)),
+                 o_mean_abs=float(err.mean()) if err.size else 0.0,
+                 n_over_1e2=int(np.count_nonzero(err > O_MAX_ABS)),
+                 n_allowance=int(np.count_nonzero(bound > O_MAX_ABS)))
+    if label is not None:
+        RECORDS.append((label, stats))
     if bad.any():
         idx = np.unravel_index(np.argmax(np.where(bad, err - bound, -np.inf)), err.shape)
         raise AssertionError(f"{what}: O error {err[idx]:.3e} > bound {bound[idx]:.3e} at {idx} "
@@ -95,6 +113,7 @@ def compare(o, lse, o_ref, lse_ref, *, bf16_out: bool, what: str = ""):
     if dl.size:
         stats["lse_max_abs"] = float(dl.max())
         stats["lse_max_rel"] = float((dl / np.maximum(np.abs(lse_ref[fin]), 1e-30)).max())
+        stats["lse_max_floor_rel"] = float((dl / np.maximum(1.0, np.abs(lse_ref[fin]))).max())
         if np.any(dl > lb):
             j = int(np.argmax(dl - lb))
             raise AssertionError(f"{what}: LSE error {dl[j]:.3e} > {lb[j]:.3e} (ref {lse_ref[fin][j]})")

@@ -183,3 +183,37 @@ def test_bwd_workspace_size():
 def test_bwd_rejected_launch_makes_no_hip_call():
     st = fa.fa_bwd(P, P, P, P, P, None, P, P, P, P, 1, 1, 16, 16, 128, 0.1, 0, None, 0, stream=0)
     assert st == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    """The Python wrappers refuse tensors that are not on the GPU before loading
+    the library or launching anything (a host pointer would be dereferenced on
+    the device)."""
+    import torch
+    q = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.attention(q, q, q, 0.125, True)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.flash_attention(q, q, q, 0.125, True)
+    lse = torch.zeros((1, 2, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.attention_bwd(q, q, q, q, lse, q, 0.125, True)
+    packed = torch.zeros((8, 2, 64), dtype=torch.bfloat16)
+    off = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        fa.attention(packed, packed, packed, 0.125, True, varlen_offsets=off, max_seqlen=8)
+
+
+def test_clock_probe_argument_checks():
+    """fa_clock_probe rejects bad arguments before any HIP call."""
+    lib = fa.load()
+    ref = ctypes.c_double(0.0)
+    bad = [(0, 10, 10, ctypes.byref(ref)),          # null samples
+           (P + 4, 10, 10, ctypes.byref(ref)),      # not 8-byte aligned
+           (P, 1, 10, ctypes.byref(ref)),           # fewer than two samples
+           (P, 1000001, 10, ctypes.byref(ref)),
+           (P, 10, 0, ctypes.byref(ref)),           # interval out of range
+           (P, 10, 100001, ctypes.byref(ref)),
+           (P, 10, 10, None)]                        # no place for the rate
+    for samples, n, us, out in bad:
+        assert lib.fa_clock_probe(samples or None, n, us, out, None) == fa.FA_ERR_INVALID_ARG

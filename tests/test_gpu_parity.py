@@ -2,8 +2,10 @@
 
 Small problems (several tiles, ragged tails, edge cases) are compared in full;
 the five measured configurations run at their full sizes in the launch
-configuration the benchmark times and are compared on sampled rows (tile and
-block edges, first/last rows, random rows) that the oracle computes one by one.
+configuration the benchmark times and are compared in full, every element of
+O and LSE; the grouped-head variant of the headline workload is compared on
+sampled rows (tile and block edges, first/last rows, random rows) that the
+oracle computes one by one.
 Both the conditional rescale (tau = 8) and the always-rescale variant (tau = 0)
 must pass.
 """
@@ -281,57 +283,46 @@ def test_grouped_full_size(tau):
     del q, k, v
     o, lse = parity.run_gpu(w, tau=tau)
     go, gl = parity.gather_rows(w, o, lse, rows)
-    stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=True, what=f"{w.name} tau={tau}")
-    print(f"{w.name} tau={tau}: {len(rows)} rows {stats}")
+    label = f"{w.name} tau={tau:g} bf16 O, {len(rows)} rows"
+    stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=True, what=label, label=label)
+    print(f"{label}: {stats}")
 
 
 # ------------------------------------------------------------ the five configurations
 
-_cache = {}
-
-
-def _config(n):
-    if n not in _cache:
-        _cache.clear()
-        w = wl.config(n)
-        rows = parity.sample_rows(w, n_random=256, seed=n)
-        q, k, v = parity.inputs_f64(w)
-        o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, w.causal, rows,
-                                               offsets=w.offsets if w.varlen else None)
-        del q, k, v
-        _cache[n] = (w, rows, o_ref, lse_ref, parity.to_device(w))
-    return _cache[n]
-
-
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("tau", [8.0, 0.0])
-def test_config(n, tau):
-    if n == 1:
-        w = wl.config(1)
-        stats = _full_check(w, tau)
-        print(f"config 1 tau={tau} f32 O: {stats}")
-        stats = _full_check(w, tau, o_dtype=0, what=w.name + "/bf16out")
-        print(f"config 1 tau={tau} bf16 O: {stats}")
-        return
-    w, rows, o_ref, lse_ref, t = _config(n)
-    # fp32 output: the arithmetic against the plain bound
-    o32, lse32 = parity.run_gpu(w, tau=tau, tensors=t, o_dtype=1)
-    go, gl = parity.gather_rows(w, o32, lse32, rows)
-    stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=False, what=f"config {n} tau={tau} f32 O")
-    print(f"config {n} tau={tau} f32 O: {len(rows)} rows {stats}")
-    del o32, lse32
-    # bf16 output: the configuration the benchmark times
-    o, lse = parity.run_gpu(w, tau=tau, tensors=t)
-    assert np.all(np.isfinite(o)), "non-finite O"
-    go, gl = parity.gather_rows(w, o, lse, rows)
-    stats = parity.compare(go, gl, o_ref, lse_ref, bf16_out=True, what=f"config {n} tau={tau}")
-    print(f"config {n} tau={tau} bf16 O: {len(rows)} rows {stats}")
-    # properties over every row: LSE finite; causal row 0 is exactly V row 0
-    assert np.all(np.isfinite(lse))
-    if w.causal:
-        v0 = wl.bf16_to_f64(w.v)
-        if w.varlen:
-            first = w.offsets[:-1].astype(np.int64)
-            assert np.array_equal(o[first], v0[first])
-        else:
-            assert np.array_equal(o[:, 0], v0[:, 0])
+def test_config(n):
+    """Every element of O and LSE of the five measured workloads, at full size in
+    the launch the benchmark times, against the fp64 oracle on the whole
+    workload: both thresholds (tau = 8 conditional, tau = 0 always), each with
+    the workload's O type and the other one (fp32 O holds the arithmetic to the
+    plain bar; bf16 O is what the benchmark times)."""
+    w = wl.config(n)
+    q, k, v = parity.inputs_f64(w)
+    if w.varlen:
+        o_ref, lse_ref = oracle.attention_varlen(q, k, v, w.offsets, w.scale, w.causal)
+    else:
+        o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
+    del q, k, v
+    t = parity.to_device(w)
+    own = 1 if w.o_dtype == "f32" else 0
+    for tau in (8.0, 0.0):
+        for o_dtype in (own, 1 - own):
+            name = "f32" if o_dtype == 1 else "bf16"
+            label = f"config {n} {w.name} tau={tau:g} {name} O"
+            print(label, flush=True)
+            o, lse = parity.run_gpu(w, tau=tau, tensors=t, o_dtype=o_dtype)
+            stats = parity.compare(o, lse, o_ref, lse_ref, bf16_out=(o_dtype == 0), what=label,
+                                   label=label)
+            print(f"{label}: {stats}", flush=True)
+            # properties over every row: LSE finite; causal row 0 is exactly V row 0
+            assert np.all(np.isfinite(lse))
+            if w.causal:
+                v0 = wl.bf16_to_f64(w.v)
+                if w.varlen:
+                    first = w.offsets[:-1].astype(np.int64)
+                    first = first[w.lengths > 0]
+                    assert np.array_equal(o[first], v0[first])
+                else:
+                    assert np.array_equal(o[:, 0], v0[:, 0])
+            del o, lse

@@ -1,0 +1,63 @@
+"""GPU unit tests of the forward kernel's row reductions (lane_pair_max,
+lane_pair_sum of fa_device.h), run in a test-only kernel that holds a score
+block in the forward kernel's accumulator layout.
+
+The vectors are the page's ("FlashAttention：一次前向计算", qingsen, section
+"how the max of one row is found across threads", table 7, and section "sum
+reduces over the same lanes"): a 64-key row whose first eight scores are
+-4 .. 3 and the rest -5 reduces to 3 on every lane; partial sums that the page
+combines in two exchange steps ((1/2, 1, 1/4, 1/4) -> (3/4, 5/4) -> 2) reduce
+to 2.  In this layout a row's keys sit on two lanes (l and l ^ 32) instead of
+four, so the page's middle step is what each half-wave holds after its in-lane
+sum, and one exchange gives 2."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kernels", "libfa_unit.so")
+
+
+@pytest.fixture(scope="module")
+def unit():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} missing: build it with tests/kernels/build.py")
+    lib = ctypes.CDLL(LIB)
+    lib.fa_unit_lane_reduce.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_unit_lane_reduce.restype = ctypes.c_int
+    return lib
+
+
+def _run(lib, S):
+    import torch
+    s = torch.from_numpy(np.ascontiguousarray(S, dtype=np.float32)).cuda()
+    out = torch.empty(128, dtype=torch.float32, device="cuda")
+    assert s.shape == (32, 64)
+    assert lib.fa_unit_lane_reduce(s.data_ptr(), out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(64, 2)
+
+
+def test_page_vectors(unit):
+    rng = np.random.default_rng(7)
+    S = rng.standard_normal((32, 64)).astype(np.float32)
+    S[0] = -5.0
+    S[0, :8] = np.arange(-4, 4)                   # table 7: max 3
+    S[1] = 0.0
+    S[1, [0, 8]] = [0.5, 0.25]                   # keys of the lower half-wave: 3/4
+    S[1, [4, 12]] = [1.0, 0.25]                   # keys of the upper half-wave: 5/4
+    got = _run(unit, S)
+    for lane in (0, 32):
+        assert got[lane, 0] == 3.0
+        assert got[lane + 1, 1] == 2.0
+    # every lane ends with its own row's maximum and sum
+    for lane in range(64):
+        row = S[lane & 31].astype(np.float64)
+        assert got[lane, 0] == row.max()
+        np.testing.assert_allclose(got[lane, 1], row.sum(), rtol=1e-5, atol=1e-5)

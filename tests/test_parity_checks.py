@@ -35,12 +35,46 @@ def test_one_element_past_the_bound_fails(ref):
     bad[0, 5, 1, 3] += 1.5e-2
     with pytest.raises(AssertionError, match="O error"):
         parity.compare(bad, lse, o, lse, bf16_out=False)
-    # with bf16 output the bound grows by half an ulp of the value, never by more
+    # with bf16 output the bar stays 1e-2 for every |O_ref| below 4 ...
     i = np.unravel_index(np.argmax(np.abs(o)), o.shape)
+    assert abs(o[i]) < parity.BF16_ALLOWANCE_FROM
     bad = o.copy()
-    bad[i] += parity.O_MAX_ABS + parity.half_ulp_bf16(o[i]) * 1.01
+    bad[i] += parity.O_MAX_ABS * 1.01
     with pytest.raises(AssertionError, match="O error"):
         parity.compare(bad, lse, o, lse, bf16_out=True)
+
+
+def test_bf16_allowance_only_from_four():
+    """The representability allowance: 1e-2 below |O_ref| = 4 (where a bf16 half
+    ulp is at most 2^-8 * 4 = 0.0078 < 1e-2), max(1e-2, half ulp + 1e-3) from 4
+    on (0.0166 in [4, 8)); elements under it are counted."""
+    o_ref = np.array([0.5, 1.5, 3.99, 4.0, 6.0, 9.0])
+    b = parity.o_bound(o_ref, bf16_out=True)
+    np.testing.assert_array_equal(b[:3], [1e-2, 1e-2, 1e-2])
+    np.testing.assert_allclose(b[3:], [2.0 ** -6 + 1e-3, 2.0 ** -6 + 1e-3, 2.0 ** -5 + 1e-3])
+    np.testing.assert_array_equal(parity.o_bound(o_ref, bf16_out=False), np.full(6, 1e-2))
+    # (padded with exact elements so the mean bound is not what decides)
+    o_ref = np.concatenate([o_ref, np.zeros(100)])
+    lse = np.zeros(o_ref.size)
+    # an error of 0.012 passes at 6.0 (allowance) and fails at 3.99 (plain bar)
+    got = o_ref.copy()
+    got[4] += 0.012
+    st = parity.compare(got, lse, o_ref, lse, bf16_out=True)
+    assert st["n_allowance"] == 3 and st["n_over_1e2"] == 1
+    got = o_ref.copy()
+    got[2] += 0.012
+    with pytest.raises(AssertionError, match="O error"):
+        parity.compare(got, lse, o_ref, lse, bf16_out=True)
+
+
+def test_labelled_comparisons_are_recorded(ref):
+    o, lse = ref
+    n = len(parity.RECORDS)
+    parity.compare(o, lse, o, lse, bf16_out=False, label="cpu check")
+    assert len(parity.RECORDS) == n + 1
+    label, st = parity.RECORDS.pop()
+    assert label == "cpu check" and st["o_max_abs"] == 0.0 and st["n_elem"] == o.size
+    assert st["lse_max_floor_rel"] == 0.0
 
 
 def test_shifted_mean_fails(ref):
