@@ -19,15 +19,16 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
+__all__ = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_TOO_LARGE",
            "FA_DTYPE_BF16", "FA_DTYPE_F32", "FA_SCHEDULE_AUTO", "FA_SCHEDULE_LINEAR",
            "FA_SCHEDULE_LPT", "FaFwdOpts", "FaError", "library_path", "load", "fa_fwd",
            "fa_fwd_ex", "fa_fwd_check", "fa_status_string", "fa_fwd_opts_default",
-           "fa_version", "fa_bwd", "fa_bwd_check", "fa_bwd_workspace_size", "fa_clock_probe",
+           "fa_version", "fa_bwd", "fa_bwd_check", "fa_bwd_workspace_size", "fa_bwd_noalloc",
+           "fa_bwd_noalloc_check", "fa_bwd_noalloc_max_bytes", "fa_clock_probe",
            "attention",
            "attention_bwd", "flash_attention"]
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, -1, -2, -3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
 FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
 FA_SCHEDULE_AUTO, FA_SCHEDULE_LINEAR, FA_SCHEDULE_LPT = 0, 1, 2
 
@@ -83,6 +84,13 @@ def load():
     lib.fa_bwd_check.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = ctypes.c_int64
+    nb = [vp] * 9 + [i, i, i, i, i, f, i, vp, i]
+    lib.fa_bwd_noalloc.argtypes = nb + [vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_check.argtypes = nb
+    lib.fa_bwd_noalloc_check.restype = i
+    lib.fa_bwd_noalloc_max_bytes.argtypes = []
+    lib.fa_bwd_noalloc_max_bytes.restype = ctypes.c_int64
     lib.fa_clock_probe.argtypes = [vp, i, i, ctypes.POINTER(ctypes.c_double), vp]
     lib.fa_clock_probe.restype = i
     _lib = lib
@@ -144,6 +152,24 @@ def fa_bwd_check(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, 
     return load().fa_bwd_check(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), B, H, Nq, Nk, d,
                                float(scale), int(causal), _ptr(varlen_offsets), int(kv_heads))
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, scale, causal,
+                   varlen_offsets=None, kv_heads=0, stream=None) -> int:
+    return load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, float(scale),
+                                 int(causal), _ptr(varlen_offsets), int(kv_heads), _stream(stream))
+
+
+def fa_bwd_noalloc_check(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, scale, causal,
+                         varlen_offsets=None, kv_heads=0) -> int:
+    return load().fa_bwd_noalloc_check(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), B, H, Nq, Nk, d, float(scale),
+                                       int(causal), _ptr(varlen_offsets), int(kv_heads))
+
+
+def fa_bwd_noalloc_max_bytes() -> int:
+    return int(load().fa_bwd_noalloc_max_bytes())
 
 
 def fa_bwd_workspace_size(B: int, H: int, Nq: int) -> int:

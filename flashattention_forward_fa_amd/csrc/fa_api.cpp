@@ -125,6 +125,34 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
                    causal, varlen_offsets, kv_heads, stream);
 }
 
+int fa_bwd_noalloc_check(const void *q, const void *k, const void *v, const void *o,
+                         const float *lse, const void *dout, const void *dq, const void *dk,
+                         const void *dv, int B, int H, int Nq, int Nk, int d, float scale,
+                         int causal, const int32_t *varlen_offsets, int kv_heads) {
+    // The workspace check of fa_bwd is passed a stand-in: D goes to the
+    // library's own array, whose size bounds the problem instead.
+    const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, (const void *)16, B, H, Nq, Nk, d,
+                             scale, causal, varlen_offsets, kv_heads);
+    if (st != FA_OK) return st;
+    if (fa_bwd_workspace_size(B, H, Nq) > fa_bwd_noalloc_max_bytes()) return FA_ERR_TOO_LARGE;
+    return FA_OK;
+}
+
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   const int32_t *varlen_offsets, int kv_heads, void *stream) {
+    const int st = fa_bwd_noalloc_check(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, scale,
+                                        causal, varlen_offsets, kv_heads);
+    if (st != FA_OK) return st;
+    void *dsum = nullptr;
+    if (fa::bwd_scratch(&dsum) != 0) return FA_ERR_HIP;
+    return run_bwd(q, k, v, o, lse, dout, dq, dk, dv, (float *)dsum, B, H, Nq, Nk, d, scale,
+                   causal, varlen_offsets, kv_heads, stream);
+}
+
+int64_t fa_bwd_noalloc_max_bytes(void) { return fa::kBwdScratchBytes; }
+
 void fa_fwd_opts_default(fa_fwd_opts *opts) {
     if (!opts) return;
     opts->o_dtype = FA_DTYPE_BF16;
@@ -227,6 +255,8 @@ const char *fa_status_string(int status) {
         case FA_ERR_INVALID_ARG: return "invalid argument";
         case FA_ERR_UNSUPPORTED: return "unsupported configuration";
         case FA_ERR_HIP: return "HIP runtime error at launch";
+        case FA_ERR_TOO_LARGE:
+            return "problem exceeds the static scratch array of fa_bwd_noalloc (use fa_bwd)";
         default: return "unknown status";
     }
 }

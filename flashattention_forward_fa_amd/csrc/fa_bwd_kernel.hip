@@ -44,6 +44,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -663,6 +664,29 @@ static int launch_bwd_d(const BwdParams &p, bool causal, hipStream_t s) {
         hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, false>), dim3(gk), dim3(kBwdThreads), 0, s, p);
     }
     return (int)hipGetLastError();
+}
+
+// The row terms D of fa_bwd_noalloc live in this device array instead of a
+// caller's workspace: each GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses the array's name as an address (on
+// the host it names a stand-in, not device memory); it uses the address
+// hipGetSymbolAddress returns for the current device, resolved once per
+// device and kept.
+static __device__ __align__(256) float scratch[kBwdScratchBytes / sizeof(float)];
+
+int bwd_scratch(void **ptr) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return -1;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return 0;
 }
 
 int launch_bwd(const BwdParams &p, int d, bool causal, void *stream) {

@@ -56,6 +56,14 @@ struct BwdParams {
 // Enqueue the backward kernels (row sums D, then dQ, then dK and dV).
 int launch_bwd(const BwdParams &p, int d, bool causal, void *stream);
 
+// The allocation-free backward keeps D (4 bytes per query row) in a static
+// device array of this size, one per GPU.
+constexpr int64_t kBwdScratchBytes = (int64_t)32 << 20;
+constexpr int kMaxDevices = 64;
+// Device address of that array on the current device (resolved once per
+// device); 0 on success, -1 if the runtime could not resolve it.
+int bwd_scratch(void **ptr);
+
 // Enqueue the clock probe: n pairs (shader clock, constant-rate clock),
 // interval_ticks of the constant-rate clock apart.
 int launch_clock_probe(uint64_t *samples, int n, unsigned interval_ticks, void *stream);

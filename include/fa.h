@@ -68,7 +68,8 @@ typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, size <= 0, bad option value */
     FA_ERR_UNSUPPORTED = -2,   /* well-formed but not implemented: d not 64/128, dtype */
-    FA_ERR_HIP = -3            /* the HIP runtime reported an error at launch */
+    FA_ERR_HIP = -3,           /* the HIP runtime reported an error at launch */
+    FA_ERR_TOO_LARGE = -4      /* fa_bwd_noalloc: the problem exceeds its static scratch array */
 } fa_status;
 
 /* Element type of O. */
@@ -175,6 +176,36 @@ int fa_bwd_check(const void *q, const void *k, const void *v, const void *o, con
                  const void *dout, const void *dq, const void *dk, const void *dv,
                  const void *workspace, int B, int H, int Nq, int Nk, int d, float scale,
                  int causal, const int32_t *varlen_offsets, int kv_heads);
+
+/*
+ * fa_bwd without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, layouts, checks and results as fa_bwd, bit for
+ * bit (the same kernels), except that the row terms D live in a static device
+ * array of the library, fa_bwd_noalloc_max_bytes() bytes (32 MiB) per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ *   - The call allocates nothing (no hipMalloc/hipFree); on a GPU's first
+ *     call it looks up the array's address there (hipGetSymbolAddress).
+ *   - It returns FA_ERR_TOO_LARGE, launching nothing, when
+ *     fa_bwd_workspace_size(B, H, Nq) exceeds that size (B*H*Nq above 2^23).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (several streams, several host threads) race and give
+ *     undefined results.  Calls in one stream order are safe; the array keeps
+ *     the last call's values, and each call writes every entry it reads.
+ */
+int fa_bwd_noalloc(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   const int32_t *varlen_offsets, int kv_heads, void *stream);
+
+/* The argument checks of fa_bwd_noalloc alone (no HIP call). */
+int fa_bwd_noalloc_check(const void *q, const void *k, const void *v, const void *o,
+                         const float *lse, const void *dout, const void *dq, const void *dk,
+                         const void *dv, int B, int H, int Nq, int Nk, int d, float scale,
+                         int causal, const int32_t *varlen_offsets, int kv_heads);
+
+/* Size in bytes of fa_bwd_noalloc's static array (the bound on 4*B*H*Nq). */
+int64_t fa_bwd_noalloc_max_bytes(void);
 
 /*
  * Diagnostics, no part of the attention computation: measure the compute-unit

@@ -217,3 +217,20 @@ def test_clock_probe_argument_checks():
            (P, 10, 10, None)]                        # no place for the rate
     for samples, n, us, out in bad:
         assert lib.fa_clock_probe(samples or None, n, us, out, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_noalloc_checks_without_a_gpu():
+    """fa_bwd_noalloc_check: the fa_bwd checks without a workspace argument, plus
+    the size bound of the static array (FA_ERR_TOO_LARGE), no HIP call."""
+    lib = fa.load()
+    cap = fa.fa_bwd_noalloc_max_bytes()
+    assert cap == 32 << 20
+    H, d = 32, 128
+    fits = cap // (4 * H)                      # 4 * H * Nq == cap
+    args = lambda Nq: (P,) * 9 + (1, H, Nq, Nq, d, 0.1, 1, None, 0)
+    assert fa.fa_bwd_noalloc_check(*args(fits)) == fa.FA_OK
+    assert fa.fa_bwd_noalloc_check(*args(fits + 1)) == fa.FA_ERR_TOO_LARGE
+    assert "scratch" in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
+    bad = (P,) * 8 + (0,) + (1, H, 100, 100, d, 0.1, 1, None, 0)   # null dv
+    assert fa.fa_bwd_noalloc_check(*bad) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_noalloc_check is not None
