@@ -8,6 +8,8 @@ namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -55,6 +57,34 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float add_bf16x2(unsigned word, float acc) {
     const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc, false);
+}
+
+// Two floats -> two fp16 (round to nearest even) in one v_cvt_pk_f16_f32.
+__device__ __forceinline__ unsigned pack_f16x2(float a, float b) {
+    const f32x2 f = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, f16x2));
+}
+
+// Sum of the two fp16 halves of a word, accumulated in fp32 (v_dot2 with (1, 1)).
+__device__ __forceinline__ float add_f16x2(unsigned word, float acc) {
+    const f16x2 ones = __builtin_bit_cast(f16x2, 0x3C003C00u);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, word), ones, acc, false);
+}
+
+// Two bf16 (one word) -> two fp16, exactly for magnitudes below 65536 (bf16
+// has 8 significant bits and fp16 11, with the wider exponent range above
+// 2^-14; bf16 values from 2^16 up become infinite).  `vmax` keeps the
+// largest magnitude seen, so the caller can tell whether any value did not fit.
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned word, float &vmax) {
+    const float lo = __uint_as_float(word << 16);
+    const float hi = __uint_as_float(word & 0xFFFF0000u);
+    vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+    return pack_f16x2(lo, hi);
+}
+
+// As bf16x2_to_f16x2 for values scaled by `sc` (a power of two) first.
+__device__ __forceinline__ unsigned bf16x2_to_f16x2_scaled(unsigned word, float sc) {
+    return pack_f16x2(__uint_as_float(word << 16) * sc, __uint_as_float(word & 0xFFFF0000u) * sc);
 }
 
 // Global loads go through buffer resources: a descriptor per K/V block whose

@@ -12,8 +12,8 @@
 //   delta  = (r - cand) * scale_log2      keep r while delta >= -tau,
 //                                         else r = cand, alpha = exp2(delta)
 //   P      = exp2(S * scale_log2 - r_safe * scale_log2)   r_safe = 0 if r = -inf
-//   l      = l * alpha + rowsum bf16(P)
-//   o      = o * alpha + bf16(P) V_j      (MFMA)
+//   l      = l * alpha + rowsum fp16(P)
+//   o      = o * alpha + fp16(P) V_j      (MFMA)
 //
 // and finally O = o / l (0 when l = 0) and LSE = ln l + r * scale ("Flash
 // Attention 4", section "rescale and write-back": valid for any consistent
@@ -23,11 +23,20 @@
 // -inf * 0 for scale 0).  A candidate of -inf (every key so far masked) keeps
 // r = -inf with alpha = 1.
 //
-// Two row sums: O is normalised by the sum of the same bf16-rounded P that the
-// PV product uses (the pages sum P before rounding it: with a stale reference
-// the dominant weight is 2^x rather than exactly 1, and summing the rounded
-// values keeps O a convex combination of the V rows), LSE by the fp32 sum of
-// the unrounded P.
+// P precision: the PV product takes fp16 operands, P rounded to fp16 as on the
+// pages and V converted from bf16 as it is staged (exact below 2^16).  bf16 P
+// (8 significant bits) is not enough for a bf16 O: with a stale reference the
+// dominant weight 2^x is rounded by up to 2^-8, which on rows dominated by one
+// or two keys adds up to ~4e-3 to O -- with the output's own rounding (up to
+// 0.0078 for |O| in [2, 4)) more than the 1e-2 bar.  A tile whose V holds a
+// finite value of 2^16 or more is computed again with V * 2^-vk (O scaled
+// back exactly), and thresholds tau > 15, where P <= 2^tau can exceed fp16,
+// use bf16 P and V.
+//
+// Two row sums: O is normalised by the sum of the same rounded P that the PV
+// product uses (the pages sum P before rounding it; summing the rounded values
+// keeps O a convex combination of the V rows), LSE by the fp32 sum of the
+// unrounded P.
 //
 // Mapping onto CDNA4 (this is not the pages' Blackwell/Hopper/Ampere design):
 //
@@ -38,7 +47,7 @@
 //   in-lane reductions plus one exchange between the two 32-lane halves
 //   (v_permlane32_swap), instead of the warp-quad shuffles of the pages.
 // * P stays in registers.  The S^T accumulator of a 32-key tile, converted to
-//   bf16, is directly the B operand (keys x queries) of O^T += V^T P^T for two
+//   fp16, is directly the B operand (keys x queries) of O^T += V^T P^T for two
 //   16-key steps.  The V^T operand comes from the row-major V tile by
 //   ds_read_b64_tr_b16 transpose reads, two per MFMA.
 // * O^T accumulates in registers with one query per lane, so the conditional
@@ -226,10 +235,11 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
 }
 
 // ------------------------------------------------------------------ kernel
-template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT>
-__global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
+template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT, bool PV16>
+__global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_kernel(FwdParams p) {
     using T = Tile<D>;
     __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::K_ELEMS + 2 * T::V_ELEMS];
+    __shared__ unsigned vmax_bits;   // workgroup max of |V| (bit pattern), overflow path only
     unsigned short *const Kbuf0 = smem;
     unsigned short *const Kbuf1 = smem + T::K_ELEMS;
     unsigned short *const Vbuf0 = smem + 2 * T::K_ELEMS;
@@ -295,15 +305,11 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         }
     }
 
+    // Row state (reset by each run of the block loop below).
     f32x16 oacc[T::NDT];
-#pragma unroll
-    for (int dt = 0; dt < T::NDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-
     unsigned nmoves = 0;     // COUNT: reference moves after the row's first live block
     float r = -INFINITY;     // exponent reference (unscaled score units)
-    float lsum = 0.f;        // this lane's half of the row sum of bf16(P) (normalises O)
+    float lsum = 0.f;        // this lane's half of the row sum of the rounded P (normalises O)
     float lsum32 = 0.f;      // ... of the fp32 P (gives LSE)
     const float c = p.scale_log2;
     const float tau = p.threshold;
@@ -377,10 +383,6 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int rr = 0; rr < KPT2; ++rr) *(u32x4 *)(Ks + k_lds[rr]) = kreg[rr];
     };
-    auto store_v = [&](unsigned short *Vs) {
-#pragma unroll
-        for (int rr = 0; rr < KPT2; ++rr) *(u32x4 *)(Vs + v_lds[rr]) = vreg[rr];
-    };
 
     // S^T = K Q^T for the BN keys of a block.
     f32x16 s[T::NKT];
@@ -414,8 +416,9 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
     };
 
-    // O^T += V^T P^T, after the conditional rescale of O by alpha.
-    bf16x8 pf[T::NKS];
+    // O^T += V^T P^T, after the conditional rescale of O by alpha.  P^T is
+    // held as raw 16-bit pairs (fp16 or bf16, the element type of the run).
+    u32x4 pf[T::NKS];
     float alpha = 1.f;
     auto rescale = [&]() {
         if (__ballot(alpha != 1.f)) {
@@ -442,21 +445,6 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
             const int col = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
             v_off[dt][h] = row * D + ((((col >> 3) ^ vswz<D>(row)) << 3) | (col & 7));
         }
-    auto pv = [&](const unsigned short *Vs) {
-#pragma unroll
-        for (int ks = 0; ks < T::NKS; ++ks) {
-#pragma unroll
-            for (int dt = 0; dt < T::NDT; ++dt) {
-                const unsigned short *a0 = Vs + 16 * ks * D;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][0]));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][1]));
-                const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, both);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[dt], 0, 0, 0);
-            }
-        }
-    };
-
     // Mask keys past the end and, for causal, after the row's last key (set
     // to -inf before the maximum).  Only blocks that cross a boundary pay.
     auto mask_block = [&](int kb) {
@@ -474,131 +462,219 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
         }
     };
 
-    // Online softmax of one masked block: row max, rescale decision,
-    // P = exp2, row sums, bf16 P; sets alpha for the accumulator.
-    auto softmax = [&]() {
-        float mx = -INFINITY;
+    // The block loop.  With PV16 the PV product takes fp16 operands (as the
+    // pages round P: 11 significant bits, so the rounding of the weights P,
+    // numerator and denominator alike, stays far below that of a bf16 O),
+    // with V converted from bf16 as it is staged, as V * 2^-vk (vk uniform,
+    // normally 0); otherwise bf16 P and V.  Returns the largest |V| staged.
+    constexpr bool F16 = PV16;
+    auto run = [&](int vk) -> float {
+        float vmax = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < T::NKT; ++kt)
+        for (int dt = 0; dt < T::NDT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-        mx = lane_pair_max(mx);
-        const float cand = fmaxf(r, mx);
-        // No live key so far (cand = -inf): keep r = -inf, alpha = 1.
-        // First live block (r = -inf): take cand, alpha = exp2(-inf) = 0.
-        // Otherwise keep r while delta = (r - cand) * c >= -tau.
-        const bool live = cand != -INFINITY;
-        const bool first = r == -INFINITY;
-        const float delta = first ? -INFINITY : (r - cand) * c;
-        const bool move = live && !(delta >= -tau);
-        if constexpr (COUNT) nmoves += (move && !first) ? 1u : 0u;
-        alpha = move ? __builtin_amdgcn_exp2f(delta) : 1.f;
-        r = move ? cand : r;
-        const float neg_rc = (r == -INFINITY) ? 0.f : -r * c;
+            for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+        nmoves = 0;
+        r = -INFINITY;
+        lsum = 0.f;
+        lsum32 = 0.f;
+        alpha = 1.f;
 
-        // P = exp2(S*c - r*c), rounded to bf16 for the PV MFMA.  The row sum
-        // for O is taken over the same bf16 values (v_dot2 with (1, 1)), so
-        // numerator and denominator see identical weights; the fp32 sum
-        // feeds LSE.  (Words are kept in scalars: a bit cast of a vector
-        // element reads element 0 in this compiler.)
-        float fsum0 = 0.f, fsum1 = 0.f;
+        auto store_v = [&](unsigned short *Vs) {
 #pragma unroll
-        for (int kt = 0; kt < T::NKT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv_ = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, neg_rc));
-                s[kt][i] = pv_;
-                if (i & 1) fsum1 += pv_; else fsum0 += pv_;
+            for (int rr = 0; rr < KPT2; ++rr) {
+                u32x4 x = vreg[rr];
+                if constexpr (F16) {
+                    if (vk == 0) {
+                        const unsigned w0 = bf16x2_to_f16x2(x[0], vmax), w1 = bf16x2_to_f16x2(x[1], vmax);
+                        const unsigned w2 = bf16x2_to_f16x2(x[2], vmax), w3 = bf16x2_to_f16x2(x[3], vmax);
+                        x = u32x4{w0, w1, w2, w3};
+                    } else {
+                        const float sc = ldexpf(1.f, -vk);
+                        const unsigned w0 = bf16x2_to_f16x2_scaled(x[0], sc), w1 = bf16x2_to_f16x2_scaled(x[1], sc);
+                        const unsigned w2 = bf16x2_to_f16x2_scaled(x[2], sc), w3 = bf16x2_to_f16x2_scaled(x[3], sc);
+                        x = u32x4{w0, w1, w2, w3};
+                    }
+                }
+                *(u32x4 *)(Vs + v_lds[rr]) = x;
             }
-        float bsum0 = 0.f, bsum1 = 0.f;
+        };
+
+        auto pv = [&](const unsigned short *Vs) {
 #pragma unroll
-        for (int ks = 0; ks < T::NKS; ++ks) {
-            const f32x16 &src = s[ks >> 1];
-            const int i0 = 8 * (ks & 1);
-            const unsigned w0 = pack_bf16x2(src[i0 + 0], src[i0 + 1]);
-            const unsigned w1 = pack_bf16x2(src[i0 + 2], src[i0 + 3]);
-            const unsigned w2 = pack_bf16x2(src[i0 + 4], src[i0 + 5]);
-            const unsigned w3 = pack_bf16x2(src[i0 + 6], src[i0 + 7]);
-            bsum0 = add_bf16x2(w0, bsum0);
-            bsum1 = add_bf16x2(w1, bsum1);
-            bsum0 = add_bf16x2(w2, bsum0);
-            bsum1 = add_bf16x2(w3, bsum1);
-            const u32x4 x = {w0, w1, w2, w3};
-            pf[ks] = __builtin_bit_cast(bf16x8, x);
+            for (int ks = 0; ks < T::NKS; ++ks) {
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; ++dt) {
+                    const unsigned short *a0 = Vs + 16 * ks * D;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][0]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][1]));
+                    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    if constexpr (F16)
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(f16x8, both), __builtin_bit_cast(f16x8, pf[ks]), oacc[dt], 0, 0, 0);
+                    else
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, both), __builtin_bit_cast(bf16x8, pf[ks]), oacc[dt], 0, 0, 0);
+                }
+            }
+        };
+
+        // Online softmax of one masked block: row max, rescale decision,
+        // P = exp2, row sums, rounded P; sets alpha for the accumulator.
+        auto softmax = [&]() {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < T::NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+            mx = lane_pair_max(mx);
+            const float cand = fmaxf(r, mx);
+            // No live key so far (cand = -inf): keep r = -inf, alpha = 1.
+            // First live block (r = -inf): take cand, alpha = exp2(-inf) = 0.
+            // Otherwise keep r while delta = (r - cand) * c >= -tau.
+            const bool live = cand != -INFINITY;
+            const bool first = r == -INFINITY;
+            const float delta = first ? -INFINITY : (r - cand) * c;
+            const bool move = live && !(delta >= -tau);
+            if constexpr (COUNT) nmoves += (move && !first) ? 1u : 0u;
+            alpha = move ? __builtin_amdgcn_exp2f(delta) : 1.f;
+            r = move ? cand : r;
+            const float neg_rc = (r == -INFINITY) ? 0.f : -r * c;
+
+            // P = exp2(S*c - r*c), rounded for the PV MFMA.  The row sum for O
+            // is taken over the same rounded values (v_dot2 with (1, 1)), so
+            // numerator and denominator see identical weights; the fp32 sum
+            // feeds LSE.  (Words are kept in scalars: a bit cast of a vector
+            // element reads element 0 in this compiler.)
+            float fsum0 = 0.f, fsum1 = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < T::NKT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float pv_ = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, neg_rc));
+                    s[kt][i] = pv_;
+                    if (i & 1) fsum1 += pv_; else fsum0 += pv_;
+                }
+            float bsum0 = 0.f, bsum1 = 0.f;
+            auto round_p = [&](auto f16c) {
+                constexpr bool H = decltype(f16c)::value;
+#pragma unroll
+                for (int ks = 0; ks < T::NKS; ++ks) {
+                    const f32x16 &src = s[ks >> 1];
+                    const int i0 = 8 * (ks & 1);
+                    unsigned w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = H ? pack_f16x2(src[i0 + 2 * e], src[i0 + 2 * e + 1])
+                                 : pack_bf16x2(src[i0 + 2 * e], src[i0 + 2 * e + 1]);
+                    bsum0 = H ? add_f16x2(w[0], bsum0) : add_bf16x2(w[0], bsum0);
+                    bsum1 = H ? add_f16x2(w[1], bsum1) : add_bf16x2(w[1], bsum1);
+                    bsum0 = H ? add_f16x2(w[2], bsum0) : add_bf16x2(w[2], bsum0);
+                    bsum1 = H ? add_f16x2(w[3], bsum1) : add_bf16x2(w[3], bsum1);
+                    pf[ks] = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            };
+            round_p(std::integral_constant<bool, F16>{});
+            lsum = lsum * alpha + (bsum0 + bsum1);
+            lsum32 = lsum32 * alpha + (fsum0 + fsum1);
+        };
+
+        // The two phases.  j ranges: M(0..n), V(-1..n-1); out-of-range parts
+        // are skipped (uniform per wave).
+        const int n = nblocks;
+        auto m_phase = [&](int j, const unsigned short *Kc, const unsigned short *Vp) {
+            const bool do_pv = j >= 1 && j <= n && active(j - 1);
+            const bool do_qk = j < n && active(j);
+            if (do_pv) rescale();
+            if (do_qk) qk(Kc);
+            if (do_pv) pv(Vp);
+        };
+        auto v_phase = [&](int j, unsigned short *Kw, unsigned short *Vw) {
+            if (j + 1 + grp < n) store_k(Kw);
+            if (j + grp < n) store_v(Vw);
+            load_k(j + 2 + grp);     // range 0 (reads nothing) past the last block
+            load_v(j + 1 + grp);
+            if (j >= 0 && j < n && active(j)) {
+                mask_block(j);
+                softmax();
+            }
+        };
+
+        if (n > 0) {
+            load_k(0);
+            store_k(Kbuf0);
+            load_k(1);
+            load_v(0);
+            __syncthreads();
+            // Group 1 starts with V(-1) (LDS writes of K_1 and V_0, loads of the
+            // next blocks) while group 0 runs M(0); from then on both groups run
+            // M(j), V(j) pairs, group 1 one phase behind.  Group 0 ends with one
+            // extra barrier so both groups meet the same number of barriers.
+            // V(j) writes K_{j+1+grp} to Kbuf[(j+1+grp)%2] and V_{j+grp} to
+            // Vbuf[(j+grp)%2].
+            unsigned short *const Kw_even = grp ? Kbuf0 : Kbuf1;   // j even
+            unsigned short *const Vw_even = grp ? Vbuf1 : Vbuf0;
+            unsigned short *const Kw_odd = grp ? Kbuf1 : Kbuf0;    // j odd
+            unsigned short *const Vw_odd = grp ? Vbuf0 : Vbuf1;
+            if constexpr (PP) {
+                if (grp == 1) {
+                    v_phase(-1, Kw_odd, Vw_odd);
+                    __syncthreads();
+                }
+                for (int j = 0; j <= n; j += 2) {
+                    m_phase(j, Kbuf0, Vbuf1);
+                    __syncthreads();
+                    v_phase(j, Kw_even, Vw_even);
+                    __syncthreads();
+                    m_phase(j + 1, Kbuf1, Vbuf0);
+                    __syncthreads();
+                    v_phase(j + 1, Kw_odd, Vw_odd);
+                    __syncthreads();
+                }
+                if (grp == 0) __syncthreads();
+            } else {
+                for (int j = 0; j <= n; j += 2) {
+                    m_phase(j, Kbuf0, Vbuf1);
+                    v_phase(j, Kw_even, Vw_even);
+                    __syncthreads();
+                    m_phase(j + 1, Kbuf1, Vbuf0);
+                    v_phase(j + 1, Kw_odd, Vw_odd);
+                    __syncthreads();
+                }
+            }
         }
-        lsum = lsum * alpha + (bsum0 + bsum1);
-        lsum32 = lsum32 * alpha + (fsum0 + fsum1);
+        return vmax;
     };
 
-    // The two phases.  j ranges: M(0..n), V(-1..n-1); out-of-range parts
-    // are skipped (uniform per wave).
-    const int n = nblocks;
-    auto m_phase = [&](int j, const unsigned short *Kc, const unsigned short *Vp) {
-        const bool do_pv = j >= 1 && j <= n && active(j - 1);
-        const bool do_qk = j < n && active(j);
-        if (do_pv) rescale();
-        if (do_qk) qk(Kc);
-        if (do_pv) pv(Vp);
-    };
-    auto v_phase = [&](int j, unsigned short *Kw, unsigned short *Vw) {
-        if (j + 1 + grp < n) store_k(Kw);
-        if (j + grp < n) store_v(Vw);
-        load_k(j + 2 + grp);     // range 0 (reads nothing) past the last block
-        load_v(j + 1 + grp);
-        if (j >= 0 && j < n && active(j)) {
-            mask_block(j);
-            softmax();
-        }
-    };
-
-    if (n > 0) {
-        load_k(0);
-        store_k(Kbuf0);
-        load_k(1);
-        load_v(0);
+    // A finite V element of magnitude 2^16 or more has no fp16 value: the tile
+    // is then computed again with V staged as V * 2^-vk, vk from the
+    // workgroup's largest |V|, and O scaled back by 2^vk (exact).  The
+    // decision is the workgroup's (every wave takes the same branch), and its
+    // barrier also orders the second run's LDS writes after the first run's
+    // reads.  (A V holding infinities keeps the first run: the rows that see
+    // them are infinite or NaN, as with exact arithmetic.)
+    int vk = 0;
+    for (;;) {   // one call site: the loop is inlined once
+        const float vmax = run(vk);
+        if (!PV16 || vk != 0) break;
+        const bool big = vmax >= 65536.f && vmax <= 3.4028235e38f;
+        if (!__builtin_amdgcn_readfirstlane(__syncthreads_or(big))) break;
+        if (tid == 0) vmax_bits = 0u;
         __syncthreads();
-        // Group 1 starts with V(-1) (LDS writes of K_1 and V_0, loads of the
-        // next blocks) while group 0 runs M(0); from then on both groups run
-        // M(j), V(j) pairs, group 1 one phase behind.  Group 0 ends with one
-        // extra barrier so both groups meet the same number of barriers.
-        // V(j) writes K_{j+1+grp} to Kbuf[(j+1+grp)%2] and V_{j+grp} to
-        // Vbuf[(j+grp)%2].
-        unsigned short *const Kw_even = grp ? Kbuf0 : Kbuf1;   // j even
-        unsigned short *const Vw_even = grp ? Vbuf1 : Vbuf0;
-        unsigned short *const Kw_odd = grp ? Kbuf1 : Kbuf0;    // j odd
-        unsigned short *const Vw_odd = grp ? Vbuf0 : Vbuf1;
-        if constexpr (PP) {
-            if (grp == 1) {
-                v_phase(-1, Kw_odd, Vw_odd);
-                __syncthreads();
-            }
-            for (int j = 0; j <= n; j += 2) {
-                m_phase(j, Kbuf0, Vbuf1);
-                __syncthreads();
-                v_phase(j, Kw_even, Vw_even);
-                __syncthreads();
-                m_phase(j + 1, Kbuf1, Vbuf0);
-                __syncthreads();
-                v_phase(j + 1, Kw_odd, Vw_odd);
-                __syncthreads();
-            }
-            if (grp == 0) __syncthreads();
-        } else {
-            for (int j = 0; j <= n; j += 2) {
-                m_phase(j, Kbuf0, Vbuf1);
-                v_phase(j, Kw_even, Vw_even);
-                __syncthreads();
-                m_phase(j + 1, Kbuf1, Vbuf0);
-                v_phase(j + 1, Kw_odd, Vw_odd);
-                __syncthreads();
-            }
-        }
+        // Non-negative floats order as their bit patterns.
+        atomicMax(&vmax_bits, __float_as_uint(vmax));
+        __syncthreads();
+        const float m = __uint_as_float(vmax_bits);
+        if (!(m <= 3.4028235e38f)) break;
+        int e;
+        (void)frexpf(m, &e);   // m < 2^e, so m * 2^-(e - 15) < 2^15
+        vk = e - 15;
     }
 
     // Epilogue: O = o / l, LSE = ln l + r * scale.
     const float l = lane_pair_sum(lsum);
     const float l32 = lane_pair_sum(lsum32);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? ldexpf(1.f / l, vk) : 0.f;
     if (row_ok) {
         OutT *Og = (OutT *)p.o + ((int64_t)tc.q_tok0 + qrow) * tok + tc.h * D;
 #pragma unroll
@@ -627,14 +703,21 @@ __global__ __launch_bounds__(Tile<D>::NT) void fa_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, bool CAUSAL, bool VARLEN, typename OutT>
-static int launch_one(const FwdParams &p, hipStream_t stream) {
-    if (p.rescale_counts)
-        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, true>), dim3(p.num_tiles),
+template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT>
+static void launch_pv(const FwdParams &p, hipStream_t stream) {
+    // fp16 P needs P <= 2^tau below fp16's largest value 65504: tau <= 15.
+    if (p.threshold <= kMaxTauF16)
+        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, COUNT, true>), dim3(p.num_tiles),
                            dim3(Tile<D>::NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, false>), dim3(p.num_tiles),
+        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, COUNT, false>), dim3(p.num_tiles),
                            dim3(Tile<D>::NT), 0, stream, p);
+}
+
+template <int D, bool CAUSAL, bool VARLEN, typename OutT>
+static int launch_one(const FwdParams &p, hipStream_t stream) {
+    if (p.rescale_counts) launch_pv<D, CAUSAL, VARLEN, OutT, true>(p, stream);
+    else                  launch_pv<D, CAUSAL, VARLEN, OutT, false>(p, stream);
     return (int)hipGetLastError();
 }
 

@@ -12,9 +12,15 @@ namespace fa {
 // (the softmax-bound head size gains from more independent waves).
 constexpr int fwd_waves(int d) { return d == 64 ? 4 : 8; }
 constexpr int fwd_block_m(int d) { return 32 * fwd_waves(d); }
+// Waves per SIMD the forward kernel is register-budgeted for: two at d = 128
+// (one 8-wave workgroup per CU), three at d = 64 (three 4-wave workgroups).
+constexpr int fwd_waves_per_simd(int d) { return d == 64 ? 3 : 2; }
 constexpr int kBlockMMax = 256;   // the largest fwd_block_m (sizes its 32-bit offsets)
 constexpr int kBlockN = 64;
 constexpr int kNumXcd = 8;   // MI355X: 8 accelerator complex dies, one L2 each
+// Largest rescale threshold for which the forward rounds P to fp16: P <= 2^tau
+// must stay below fp16's largest finite value (65504); above it P is bf16.
+constexpr float kMaxTauF16 = 15.0f;
 
 enum class OutType : int { BF16 = 0, F32 = 1 };
 

@@ -118,6 +118,59 @@ def test_scale_values(scale):
     _full_check(w, 8.0, o_dtype=1)
 
 
+def _scaled_v(w, k, heads=None):
+    """The workload with V multiplied by 2^k (exact in bf16), on every head or on `heads`."""
+    import dataclasses
+    v = wl.bf16_to_f32(w.v)
+    if heads is None:
+        v = v * np.float32(2.0 ** k)
+    else:
+        v[..., heads, :] *= np.float32(2.0 ** k)
+    return dataclasses.replace(w, v=wl.bf16_bits(v))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_v_beyond_fp16_range(d):
+    """V values of magnitude 2^16 and more have no fp16 value: such a tile is
+    computed again with V staged as V * 2^-vk, and O scaled back.  Scaling V by
+    2^20 must scale O by exactly 2^20 (fp32 and bf16 O), and the result must
+    match the oracle relative to max |V|; heads whose V stays small are
+    untouched by another head's rerun."""
+    import dataclasses
+    w = wl.make_fixed(1, 3, 300, 300, d, seed=88, causal=True)
+    # no |v| below 2^-8: tiny values are fp16 subnormals unscaled but normal
+    # scaled, which would round them differently
+    v = wl.bf16_to_f32(w.v)
+    v = np.where(np.abs(v) < 2.0 ** -8, np.copysign(np.float32(2.0 ** -8), v), v)
+    w = dataclasses.replace(w, v=wl.bf16_bits(v.astype(np.float32)))
+    big = _scaled_v(w, 20)
+    for o_dtype in (1, 0):
+        o0, l0 = parity.run_gpu(w, o_dtype=o_dtype)
+        o1, l1 = parity.run_gpu(big, o_dtype=o_dtype)
+        assert np.array_equal(o1, o0 * 2.0 ** 20), o_dtype
+        assert np.array_equal(l1, l0)
+    q, k, v = parity.inputs_f64(big)
+    o_ref, lse_ref = oracle.attention(q, k, v, big.scale, big.causal)
+    o1, l1 = parity.run_gpu(big, o_dtype=1)
+    vmax = float(np.abs(v).max())
+    assert np.abs(o1 - o_ref).max() <= 1e-2 * vmax / 4.0
+    # one head's huge V: the other heads give what they give without it
+    mixed = _scaled_v(w, 20, heads=[1])
+    om, lm = parity.run_gpu(mixed, o_dtype=1)
+    o0, l0 = parity.run_gpu(w, o_dtype=1)
+    assert np.array_equal(om[:, :, [0, 2]], o0[:, :, [0, 2]])
+    assert np.array_equal(om[:, :, 1], o0[:, :, 1] * 2.0 ** 20)
+
+
+def test_tau_above_fp16_range_uses_bf16_p():
+    """tau > 15 (P up to 2^tau would overflow fp16) rounds P to bf16: results
+    still meet the bar in fp32 O, and tau = 15 (the largest fp16 threshold)
+    too."""
+    w = wl.make_fixed(1, 4, 500, 500, 128, seed=89, causal=True)
+    for tau in (15.0, 16.0, 40.0):
+        _full_check(w, tau, o_dtype=1, what=f"{w.name} tau={tau} f32 O")
+
+
 def test_small_varlen_full():
     w = wl.make_varlen(3, 64, seed=31, nseq=5, len_lo=1, len_hi=700)
     _full_check(w, 8.0)
