@@ -73,13 +73,9 @@ __device__ __forceinline__ float add_f16x2(unsigned word, float acc) {
 
 // Two bf16 (one word) -> two fp16, exactly for magnitudes below 65536 (bf16
 // has 8 significant bits and fp16 11, with the wider exponent range above
-// 2^-14; bf16 values from 2^16 up become infinite).  `vmax` keeps the
-// largest magnitude seen, so the caller can tell whether any value did not fit.
-__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned word, float &vmax) {
-    const float lo = __uint_as_float(word << 16);
-    const float hi = __uint_as_float(word & 0xFFFF0000u);
-    vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
-    return pack_f16x2(lo, hi);
+// 2^-14; bf16 values from 2^16 up become infinite).
+__device__ __forceinline__ unsigned bf16x2_to_f16x2(unsigned word) {
+    return pack_f16x2(__uint_as_float(word << 16), __uint_as_float(word & 0xFFFF0000u));
 }
 
 // As bf16x2_to_f16x2 for values scaled by `sc` (a power of two) first.

@@ -466,10 +466,9 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     // pages round P: 11 significant bits, so the rounding of the weights P,
     // numerator and denominator alike, stays far below that of a bf16 O),
     // with V converted from bf16 as it is staged, as V * 2^-vk (vk uniform,
-    // normally 0); otherwise bf16 P and V.  Returns the largest |V| staged.
+    // normally 0); otherwise bf16 P and V.
     constexpr bool F16 = PV16;
-    auto run = [&](int vk) -> float {
-        float vmax = 0.f;
+    auto run = [&](int vk) {
 #pragma unroll
         for (int dt = 0; dt < T::NDT; ++dt)
 #pragma unroll
@@ -486,9 +485,8 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
                 u32x4 x = vreg[rr];
                 if constexpr (F16) {
                     if (vk == 0) {
-                        const unsigned w0 = bf16x2_to_f16x2(x[0], vmax), w1 = bf16x2_to_f16x2(x[1], vmax);
-                        const unsigned w2 = bf16x2_to_f16x2(x[2], vmax), w3 = bf16x2_to_f16x2(x[3], vmax);
-                        x = u32x4{w0, w1, w2, w3};
+                        x = u32x4{bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]),
+                                  bf16x2_to_f16x2(x[3])};
                     } else {
                         const float sc = ldexpf(1.f, -vk);
                         const unsigned w0 = bf16x2_to_f16x2_scaled(x[0], sc), w1 = bf16x2_to_f16x2_scaled(x[1], sc);
@@ -643,29 +641,47 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
                 }
             }
         }
-        return vmax;
     };
 
-    // A finite V element of magnitude 2^16 or more has no fp16 value: the tile
-    // is then computed again with V staged as V * 2^-vk, vk from the
-    // workgroup's largest |V|, and O scaled back by 2^vk (exact).  The
-    // decision is the workgroup's (every wave takes the same branch), and its
-    // barrier also orders the second run's LDS writes after the first run's
-    // reads.  (A V holding infinities keeps the first run: the rows that see
-    // them are infinite or NaN, as with exact arithmetic.)
+    // A finite V element of magnitude 2^16 or more has no fp16 value; it
+    // becomes infinite, and since the PV product multiplies it by every row's
+    // P (infinite for P > 0, NaN for P = 0), it leaves a non-finite value in
+    // the accumulator of every row of the tile that visits its block -- which
+    // finite inputs below 2^16 cannot (|P| <= 2^15).  Such a tile is computed
+    // again with V staged as V * 2^-vk, vk from the largest |V| of its K/V
+    // blocks (a separate pass over them), and O scaled back by 2^vk (exact).
+    // The decision is the workgroup's (every wave takes the same branch), and
+    // its barrier also orders the second run's LDS writes after the first
+    // run's reads.  A V holding infinities or NaN keeps the first result: the
+    // rows that see them are infinite or NaN, as with exact arithmetic.
     int vk = 0;
     for (;;) {   // one call site: the loop is inlined once
-        const float vmax = run(vk);
+        run(vk);
         if (!PV16 || vk != 0) break;
-        const bool big = vmax >= 65536.f && vmax <= 3.4028235e38f;
-        if (!__builtin_amdgcn_readfirstlane(__syncthreads_or(big))) break;
+        float t = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < T::NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t += oacc[dt][i];
+        if (!__builtin_amdgcn_readfirstlane(__syncthreads_or(!(fabsf(t) <= 3.4028235e38f)))) break;
+        // Largest |V| over the tile's K/V blocks (rows past Nk read as 0).
+        float vmax = 0.f;
+        for (int kb = 0; kb < nblocks; ++kb) {
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)kb * T::BN * tkv, block_bytes(kb));
+            for (int u = tid; u < T::BN * D / 8; u += T::NT) {
+                const u32x4 x = buffer_load16(rv, (unsigned)(u / (D / 8)) * tkvb + 16u * (u % (D / 8)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    vmax = fmaxf(vmax, fmaxf(fabsf(__uint_as_float(x[e] << 16)),
+                                             fabsf(__uint_as_float(x[e] & 0xFFFF0000u))));
+            }
+        }
         if (tid == 0) vmax_bits = 0u;
         __syncthreads();
-        // Non-negative floats order as their bit patterns.
-        atomicMax(&vmax_bits, __float_as_uint(vmax));
+        atomicMax(&vmax_bits, __float_as_uint(vmax));   // non-negative floats order as their bits
         __syncthreads();
         const float m = __uint_as_float(vmax_bits);
-        if (!(m <= 3.4028235e38f)) break;
+        if (!(m >= 65536.f && m <= 3.4028235e38f)) break;
         int e;
         (void)frexpf(m, &e);   // m < 2^e, so m * 2^-(e - 15) < 2^15
         vk = e - 15;
