@@ -46,7 +46,22 @@ class FaFwdOpts(ctypes.Structure):
     """Mirror of ``fa_fwd_opts`` in include/fa.h."""
     _fields_ = [("o_dtype", ctypes.c_int32), ("rescale_threshold", ctypes.c_float),
                 ("schedule", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
-                ("rescale_counts", ctypes.c_void_p)]
+                ("rescale_counts", ctypes.c_void_p), ("trace", ctypes.c_void_p),
+                ("trace_workgroups", ctypes.c_int32)]
+
+
+def _bind_torch_hip_runtime():
+    """Import torch before the library is loaded.  torch brings its own HIP
+    runtime and asks for it by an unversioned name; libfa asks for
+    libamdhip64.so.7.  Loaded after torch, libfa binds to torch's runtime (same
+    SONAME); loaded first, it would pull in the system runtime, torch would
+    then load its own beside it, and launches from libfa would go to a runtime
+    that does not own torch's memory and streams.  Without torch there is only
+    the system runtime and nothing to do."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
 
 
 def library_path() -> str:
@@ -62,6 +77,7 @@ def load():
     if not os.path.exists(path):
         raise RuntimeError(f"libfa.so not found at {path}; build it with "
                            f"`python -m flashattention_forward_fa_amd.build`")
+    _bind_torch_hip_runtime()
     lib = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     common = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]

@@ -35,19 +35,26 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libfa.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCES, "-o", tmp]
+LIB_TRACE = os.path.join(HERE, "libfa_trace.so")
+
+
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compile every source into libfa.so (always recompiles); trace=True builds
+    the timeline flavour libfa_trace.so instead (FA_TRACE: the forward kernel
+    records shader-clock stamps at its phase boundaries into opts.trace)."""
+    lib = LIB_TRACE if trace else LIB
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *(["-DFA_TRACE"] if trace else []), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     # Resolve every symbol now: a kernel whose launch stub the host pass did
     # not emit would otherwise only fail when the library is loaded.
     ctypes.CDLL(tmp, mode=os.RTLD_NOW)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, trace="--trace" in sys.argv[1:]))

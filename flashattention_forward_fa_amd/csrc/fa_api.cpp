@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 400;   // 0.4.0: per-row rescale counts (fa_fwd_opts.rescale_counts)
+constexpr int kVersion = 500;   // 0.5.0: fp16 P, fa_bwd_noalloc, the trace fields of fa_fwd_opts
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -32,6 +32,13 @@ int check_args(const void *q, const void *k, const void *v, const void *o, const
     if (opts.kv_heads < 0 || opts.kv_heads > H || (opts.kv_heads > 0 && H % opts.kv_heads != 0))
         return FA_ERR_INVALID_ARG;
     if ((uintptr_t)opts.rescale_counts & 3u) return FA_ERR_INVALID_ARG;
+    if (opts.trace) {
+#ifdef FA_TRACE
+        if (((uintptr_t)opts.trace & 7u) || opts.trace_workgroups < 1) return FA_ERR_INVALID_ARG;
+#else
+        return FA_ERR_UNSUPPORTED;   // only the timeline build records
+#endif
+    }
     if (opts.o_dtype != FA_DTYPE_BF16 && opts.o_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (offsets) {
@@ -160,6 +167,8 @@ void fa_fwd_opts_default(fa_fwd_opts *opts) {
     opts->schedule = FA_SCHEDULE_AUTO;
     opts->kv_heads = 0;
     opts->rescale_counts = nullptr;
+    opts->trace = nullptr;
+    opts->trace_workgroups = 0;
 }
 
 int fa_fwd_check(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -216,6 +225,8 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
     }
     p.threshold = op.rescale_threshold;
     p.rescale_counts = op.rescale_counts;
+    p.trace = op.trace;
+    p.trace_workgroups = op.trace ? op.trace_workgroups : 0;
 
     // Clear a stale error so the status below belongs to this launch.
     (void)hipGetLastError();

@@ -50,7 +50,7 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
-namespace fa {
+FA_NS_BEGIN
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
@@ -695,4 +695,4 @@ int launch_bwd(const BwdParams &p, int d, bool causal, void *stream) {
     return launch_bwd_d<128>(p, causal, s);
 }
 
-}  // namespace fa
+FA_NS_END  // namespace fa

@@ -13,7 +13,7 @@
 
 #include "fa_internal.h"
 
-namespace fa {
+FA_NS_BEGIN
 
 __global__ __launch_bounds__(64) void fa_clock_probe_kernel(uint64_t *out, int n, unsigned interval) {
     if (threadIdx.x != 0) return;
@@ -40,4 +40,4 @@ int launch_clock_probe(uint64_t *samples, int n, unsigned interval_ticks, void *
     return (int)hipGetLastError();
 }
 
-}  // namespace fa
+FA_NS_END  // namespace fa

@@ -1,10 +1,12 @@
 // fa_device.h -- device helpers shared by the forward and backward kernels.
 #pragma once
 
+#include "fa_ns.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace fa {
+FA_NS_BEGIN
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -95,4 +97,4 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigne
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
-}  // namespace fa
+FA_NS_END  // namespace fa

@@ -81,7 +81,7 @@
 #include "fa_device.h"
 #include "fa_internal.h"
 
-namespace fa {
+FA_NS_BEGIN
 
 template <int D_>
 struct Tile {
@@ -248,6 +248,26 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     TileCoord tc;
     const bool ok = VARLEN ? decode_varlen<T::BM>(blockIdx.x, p, tc) : decode_fixed(blockIdx.x, p, tc);
     if (!ok) return;   // uniform over the workgroup
+
+#ifdef FA_TRACE
+    // Timeline build: lane 0 of waves 0 and 4 (one per ping-pong group) of the
+    // first trace_workgroups workgroups records (event code << 56 | shader
+    // clock) at every phase boundary into p.trace, kTraceEvents slots per
+    // wave.  Reading the clock waits for this wave's outstanding LDS and
+    // scalar operations, so the build is a measurement tool, not the product.
+    uint64_t *trace_out = nullptr;
+    int trace_n = 0;
+    if (p.trace && (int)blockIdx.x < p.trace_workgroups && (threadIdx.x & 63) == 0 &&
+        ((threadIdx.x >> 6) & 3) == 0)
+        trace_out = p.trace + ((int64_t)blockIdx.x * 2 + (threadIdx.x >> 8)) * kTraceEvents;
+    auto mark = [&](unsigned code) {
+        if (trace_out && trace_n < kTraceEvents)
+            trace_out[trace_n++] = ((uint64_t)code << 56) | ((uint64_t)clock64() & 0x00FFFFFFFFFFFFFFull);
+    };
+#else
+    auto mark = [](unsigned) {};
+#endif
+    mark(kTraceStart);
 
     const int tid = threadIdx.x;
     // Wave index, known wave-uniform (SGPR): keeps per-wave decisions and
@@ -583,19 +603,25 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
         auto m_phase = [&](int j, const unsigned short *Kc, const unsigned short *Vp) {
             const bool do_pv = j >= 1 && j <= n && active(j - 1);
             const bool do_qk = j < n && active(j);
+            mark(kTraceMBegin);
             if (do_pv) rescale();
             if (do_qk) qk(Kc);
             if (do_pv) pv(Vp);
+            mark(kTraceMEnd);
         };
         auto v_phase = [&](int j, unsigned short *Kw, unsigned short *Vw) {
+            mark(kTraceVBegin);
             if (j + 1 + grp < n) store_k(Kw);
             if (j + grp < n) store_v(Vw);
+            mark(kTraceVStored);
             load_k(j + 2 + grp);     // range 0 (reads nothing) past the last block
             load_v(j + 1 + grp);
+            mark(kTraceVLoaded);
             if (j >= 0 && j < n && active(j)) {
                 mask_block(j);
                 softmax();
             }
+            mark(kTraceVEnd);
         };
 
         if (n > 0) {
@@ -687,6 +713,7 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
         vk = e - 15;
     }
 
+    mark(kTraceLoopEnd);
     // Epilogue: O = o / l, LSE = ln l + r * scale.
     const float l = lane_pair_sum(lsum);
     const float l32 = lane_pair_sum(lsum32);
@@ -717,6 +744,7 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
             if constexpr (COUNT) p.rescale_counts[idx] = nmoves;
         }
     }
+    mark(kTraceEnd);
 }
 
 template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT>
@@ -757,5 +785,5 @@ int launch_fwd(const FwdParams &p, int d, bool causal, OutType out, void *stream
     return launch_d<128>(p, causal, out, s);
 }
 
-}  // namespace fa
+FA_NS_END  // namespace fa
 

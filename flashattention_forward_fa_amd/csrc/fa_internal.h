@@ -1,9 +1,11 @@
 // fa_internal.h -- what the C-ABI layer hands to the kernel launcher.
 #pragma once
 
+#include "fa_ns.h"
+
 #include <stdint.h>
 
-namespace fa {
+FA_NS_BEGIN
 
 // Tile shape of the forward kernel: a workgroup of fwd_waves(d) wavefronts
 // owns fwd_block_m(d) = 32 * fwd_waves(d) query rows (32 per wave); K/V stream
@@ -43,6 +45,15 @@ struct FwdParams {
     float scale_log2;         // exponent scale: |s| * log2(e) rounded once (1 when s = 0)
     float threshold;          // tau
     uint32_t *rescale_counts; // nullptr, or per-row counts of reference moves (layout of lse)
+    uint64_t *trace;          // timeline build only: event stamps, kTraceEvents per traced wave
+    int trace_workgroups;     // ... of the first trace_workgroups workgroups (waves 0 and 4)
+};
+
+// Timeline events (the trace build): code << 56 | shader clock.
+constexpr int kTraceEvents = 1024;
+enum TraceEvent : unsigned {
+    kTraceStart = 1, kTraceMBegin = 2, kTraceMEnd = 3, kTraceVBegin = 4, kTraceVStored = 5,
+    kTraceVLoaded = 6, kTraceVEnd = 7, kTraceLoopEnd = 8, kTraceEnd = 9
 };
 
 // Enqueue the forward kernel; returns a hipError_t value (0 = success).
@@ -74,4 +85,4 @@ int bwd_scratch(void **ptr);
 // interval_ticks of the constant-rate clock apart.
 int launch_clock_probe(uint64_t *samples, int n, unsigned interval_ticks, void *stream);
 
-}  // namespace fa
+FA_NS_END  // namespace fa

@@ -105,6 +105,16 @@ typedef enum fa_schedule {
  *                       delta < -tau).  Diagnostics: the computation and the
  *                       other outputs are the same; without it the kernels
  *                       carry no counting code.
+ *   trace, trace_workgroups : NULL / 0 (the defaults).  Only the timeline
+ *                       build of the library (libfa_trace.so, compiled with
+ *                       FA_TRACE) accepts a trace buffer: device memory,
+ *                       8-byte aligned, of trace_workgroups * 2 * 1024 uint64,
+ *                       owned by the caller.  Lane 0 of waves 0 and 4 of each
+ *                       of the first trace_workgroups workgroups writes up to
+ *                       1024 stamps (event << 56 | shader clock) at the phase
+ *                       boundaries of the block loop; unused slots keep their
+ *                       contents.  The default library returns
+ *                       FA_ERR_UNSUPPORTED for a non-NULL trace.
  */
 typedef struct fa_fwd_opts {
     int32_t o_dtype;
@@ -112,10 +122,12 @@ typedef struct fa_fwd_opts {
     int32_t schedule;
     int32_t kv_heads;
     uint32_t *rescale_counts;
+    uint64_t *trace;
+    int32_t trace_workgroups;
 } fa_fwd_opts;
 
 /* Fill *opts with the defaults (bf16 O, tau = 8, automatic schedule, Hkv = H,
- * no rescale counts). */
+ * no rescale counts, no trace). */
 void fa_fwd_opts_default(fa_fwd_opts *opts);
 
 /*

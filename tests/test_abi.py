@@ -234,3 +234,18 @@ def test_noalloc_checks_without_a_gpu():
     bad = (P,) * 8 + (0,) + (1, H, 100, 100, d, 0.1, 1, None, 0)   # null dv
     assert fa.fa_bwd_noalloc_check(*bad) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_bwd_noalloc_check is not None
+
+
+def test_library_binds_after_torch():
+    """Loading the library imports torch first, so libfa resolves the HIP
+    runtime torch already loaded instead of a second copy (checked here from
+    the process's mapped libraries: exactly one libamdhip64 after load)."""
+    import subprocess
+    import sys
+    code = ("import flashattention_forward_fa_amd as fa; fa.load(); "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1"
