@@ -11,14 +11,19 @@ Timing: first a settle phase of back-to-back launches until --settle-ms of
 wall time have passed (the shader clock of a cold GPU takes a few hundred
 milliseconds of load to reach its steady value, whatever --warmup says), then
 --warmup untimed steps, then exactly --steps timed steps between two
-synchronisations.  While those run, a one-wavefront probe on a second stream
-samples the shader clock against the constant-rate clock (fa_clock_probe), so
-the line states the clock the throughput was measured at.
+synchronisations.  Right after them the same launches run once more, now with
+a one-wavefront probe on a second stream sampling the shader clock against the
+constant-rate clock (fa_clock_probe), so the line states the clock the
+throughput was measured at.  (The probe holds registers on one compute unit,
+where a workgroup of the d = 128 kernel then no longer fits; beside the timed
+loop it slowed it by about 6%, so it samples an adjacent window of the same
+load instead.)
 
 Prints one JSON line:
   value        TFLOP/s = 4*B*H*Nq*Nk*d/2 (causal) / ms_per_step
-  roofline     the kernel's achieved TFLOP/s from per-launch HIP events on the
-               launch stream (a second loop of K launches), against the bf16
+  roofline     the kernel's achieved TFLOP/s from the average launch duration
+               over the timed region (two HIP events on the launch stream
+               bracketing the K launches), against the bf16
                dense MFMA peak (2.5 PFLOP/s, nominal at 2.4 GHz), and against
                CUs x 4096 flop/clk x the measured shader clock (peak_at_sclk);
                traffic = HBM bytes per launch from the committed rocprofv3
@@ -241,46 +246,43 @@ def main():
         settle_ms = (time.perf_counter() - t0) * 1e3
         if settle_ms >= args.settle_ms:
             break
-    est_ms = settle_ms / settle_launches
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # The whole job: K steps back to back, wall clock between two syncs; the
-    # clock probe samples for about 90% of the expected duration beside them.
+    # The whole job: K steps back to back, wall clock between two syncs, and
+    # two HIP events on the launch stream bracketing the same K launches (the
+    # kernel's average launch duration back to back, for the roofline).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    avg_launch_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # The shader clock under the same load: K more launches with the probe
+    # sampling beside them for about 90% of their expected duration.
     probe_interval_us = 10
-    n_probe = max(2, min(1000000, int(0.9 * est_ms * args.steps * 1e3 / probe_interval_us)))
+    n_probe = max(2, min(1000000, int(0.9 * ms_per_step * args.steps * 1e3 / probe_interval_us)))
     samples = torch.zeros(2 * n_probe, dtype=torch.int64, device="cuda")
     side = torch.cuda.Stream()
     torch.cuda.synchronize()
     st_probe, ref_hz = fa.fa_clock_probe(samples, n_probe, probe_interval_us, side)
     if st_probe != fa.FA_OK:
         raise fa.FaError(st_probe, "fa_clock_probe")
-    t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
     sm = samples.cpu().numpy().astype(np.float64).reshape(-1, 2)
     sclk_ghz = float((sm[-1, 0] - sm[0, 0]) / (sm[-1, 1] - sm[0, 1]) * ref_hz / 1e9)
     probe_ms = float((sm[-1, 1] - sm[0, 1]) / ref_hz * 1e3)
-
-    # The kernel: K more launches, each bracketed by HIP events recorded on
-    # the launch stream (the events add small gaps, so this loop is not the
-    # one that gives `value`).
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
-    sorted_ms = sorted(launch_ms)
-    median_launch_ms = sorted_ms[len(sorted_ms) // 2]
 
     flops = w.flops() * (2.5 if args.backward else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -322,8 +324,6 @@ def main():
                      "frac_at_sclk": round(achieved / peak_at_sclk, 4),
                      "cus": cus,
                      "avg_launch_ms": round(avg_launch_ms, 5),
-                     "median_launch_ms": round(median_launch_ms, 5),
-                     "min_launch_ms": round(sorted_ms[0], 5),
                      "algorithmic_hbm_bytes": w.io_bytes()},
     }
     if args.cpu_seconds > 0:
