@@ -156,6 +156,8 @@ def main():
                     help="launch back to back for at least this long before the warm-up (clocks)")
     ap.add_argument("--config", type=int, default=3, help="workload 1-5 (3 = the headline)")
     ap.add_argument("--tau", type=float, default=8.0, help="rescale threshold")
+    ap.add_argument("--exp2-poly", type=int, default=0,
+                    help="exponentials per 16 by the FMA polynomial (0 = all by v_exp_f32, or 8)")
     ap.add_argument("--backward", action="store_true",
                     help="time fa_bwd (dQ, dK, dV for the forward's outputs) instead of fa_fwd")
     ap.add_argument("--kv-heads", type=int, default=0,
@@ -209,6 +211,7 @@ def main():
     opts.o_dtype = odt
     opts.rescale_threshold = args.tau
     opts.kv_heads = w.kv_heads
+    opts.exp2_poly = args.exp2_poly
     stream = torch.cuda.current_stream()
 
     def step():
@@ -292,8 +295,9 @@ def main():
     traffic = None if args.backward else traffic_from_profile(w.name)
     # The headline metric names its workload; another --config or --kv-heads names its own.
     metric = "attention fwd TFLOP/s and % of bf16 MFMA peak (d=128, N=4096 causal)"
-    if args.config != 3 or args.kv_heads:
-        metric = f"attention fwd TFLOP/s and % of bf16 MFMA peak ({w.name})"
+    if args.config != 3 or args.kv_heads or args.exp2_poly:
+        poly = f", exp2 polynomial {args.exp2_poly}/16" if args.exp2_poly else ""
+        metric = f"attention fwd TFLOP/s and % of bf16 MFMA peak ({w.name}{poly})"
     if args.backward:
         metric = ("attention bwd TFLOP/s (algorithmic flops 2.5x the forward's: five products) "
                   f"and % of bf16 MFMA peak ({w.name})")
@@ -312,7 +316,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) bf16 Q/K/V",
-        "config": {**w.describe(), "rescale_threshold": args.tau,
+        "config": {**w.describe(), "rescale_threshold": args.tau, "exp2_poly": args.exp2_poly,
                    "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
                    "flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

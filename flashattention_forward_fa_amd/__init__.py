@@ -47,7 +47,7 @@ class FaFwdOpts(ctypes.Structure):
     _fields_ = [("o_dtype", ctypes.c_int32), ("rescale_threshold", ctypes.c_float),
                 ("schedule", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
                 ("rescale_counts", ctypes.c_void_p), ("trace", ctypes.c_void_p),
-                ("trace_workgroups", ctypes.c_int32)]
+                ("trace_workgroups", ctypes.c_int32), ("exp2_poly", ctypes.c_int32)]
 
 
 def _bind_torch_hip_runtime():
@@ -232,7 +232,8 @@ def _same_gpu(**tensors):
 
 def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_seqlen=None,
               o_dtype=FA_DTYPE_BF16, rescale_threshold: float = 8.0,
-              schedule: int = FA_SCHEDULE_AUTO, stream=None, rescale_counts: bool = False):
+              schedule: int = FA_SCHEDULE_AUTO, stream=None, rescale_counts: bool = False,
+              exp2_poly: int = 0):
     """Allocate O and LSE with torch on q's device and run fa_fwd_ex.
 
     Fixed length: q [B,Nq,H,d], k/v [B,Nk,Hkv,d] bf16 -> o [B,Nq,H,d], lse [B,H,Nq].
@@ -276,6 +277,7 @@ def attention(q, k, v, scale: float, causal: bool, *, varlen_offsets=None, max_s
     opts.rescale_threshold = rescale_threshold
     opts.schedule = schedule
     opts.kv_heads = Hkv
+    opts.exp2_poly = exp2_poly
     counts = None
     if rescale_counts:
         counts = torch.zeros(lse.shape, dtype=torch.int32, device=q.device)

@@ -40,6 +40,12 @@ int check_args(const void *q, const void *k, const void *v, const void *o, const
 #endif
     }
     if (opts.o_dtype != FA_DTYPE_BF16 && opts.o_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    if (opts.exp2_poly != 0) {
+        if (opts.exp2_poly != 4 && opts.exp2_poly != 8 && opts.exp2_poly != 16) return FA_ERR_UNSUPPORTED;
+        if (opts.rescale_threshold > fa::kMaxTauF16 || opts.rescale_counts ||
+            opts.o_dtype != FA_DTYPE_BF16)
+            return FA_ERR_UNSUPPORTED;
+    }
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (offsets) {
         if ((uintptr_t)offsets & 3u) return FA_ERR_INVALID_ARG;
@@ -169,6 +175,7 @@ void fa_fwd_opts_default(fa_fwd_opts *opts) {
     opts->rescale_counts = nullptr;
     opts->trace = nullptr;
     opts->trace_workgroups = 0;
+    opts->exp2_poly = 0;
 }
 
 int fa_fwd_check(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -227,6 +234,7 @@ int fa_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
     p.rescale_counts = op.rescale_counts;
     p.trace = op.trace;
     p.trace_workgroups = op.trace ? op.trace_workgroups : 0;
+    p.exp2_poly = op.exp2_poly;
 
     // Clear a stale error so the status below belongs to this launch.
     (void)hipGetLastError();

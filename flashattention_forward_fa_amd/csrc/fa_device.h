@@ -85,6 +85,25 @@ __device__ __forceinline__ unsigned bf16x2_to_f16x2_scaled(unsigned word, float 
     return pack_f16x2(__uint_as_float(word << 16) * sc, __uint_as_float(word & 0xFFFF0000u) * sc);
 }
 
+// 2^x without the transcendental unit: 2^j * p(f), j = floor(x), f = x - j in
+// [0, 1), with p the degree-3 polynomial of least relative error on [0, 1]
+// (Remez exchange; csrc/fit_exp2_poly.py prints these coefficients and the
+// bound, 7.48e-5) and 2^j applied to the exponent field (v_ldexp_f32).  For
+// the forward's split exp2 ("Flash Attention 4", section "algorithm
+// structure": part of a block's exponentials on the FMA pipes).  x is clamped
+// at -200 so -inf (masked scores) gives exactly 0; a NaN x also gives 0.
+constexpr float kExp2C0 = 0.99992521856271555f;
+constexpr float kExp2C1 = 0.69583354049475288f;
+constexpr float kExp2C2 = 0.22606715542748335f;
+constexpr float kExp2C3 = 0.078024522640479307f;
+
+__device__ __forceinline__ float exp2_poly(float x) {
+    x = fmaxf(x, -200.f);
+    const float f = __builtin_amdgcn_fractf(x);   // x - floor(x), v_fract_f32
+    const float p = fmaf(fmaf(fmaf(kExp2C3, f, kExp2C2), f, kExp2C1), f, kExp2C0);
+    return ldexpf(p, (int)floorf(x));
+}
+
 // Global loads go through buffer resources: a descriptor per K/V block whose
 // range ends at the block's last valid key, so keys past the end read as 0
 // with no branch and no address arithmetic per block.

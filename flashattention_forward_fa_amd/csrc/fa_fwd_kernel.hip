@@ -235,7 +235,7 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
 }
 
 // ------------------------------------------------------------------ kernel
-template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT, bool PV16>
+template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT, bool PV16, int EP>
 __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_kernel(FwdParams p) {
     using T = Tile<D>;
     __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::K_ELEMS + 2 * T::V_ELEMS];
@@ -569,7 +569,11 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
             for (int kt = 0; kt < T::NKT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float pv_ = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, neg_rc));
+                    // EP of a lane's 16 exponentials per 32-key tile (every
+                    // 16/EP-th) by the FMA polynomial, the rest by v_exp_f32.
+                    const float xa = fmaf(s[kt][i], c, neg_rc);
+                    const bool poly = EP > 0 && (i * EP) % 16 < EP;
+                    const float pv_ = poly ? exp2_poly(xa) : __builtin_amdgcn_exp2f(xa);
                     s[kt][i] = pv_;
                     if (i & 1) fsum1 += pv_; else fsum0 += pv_;
                 }
@@ -750,12 +754,24 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
 template <int D, bool CAUSAL, bool VARLEN, typename OutT, bool COUNT>
 static void launch_pv(const FwdParams &p, hipStream_t stream) {
     // fp16 P needs P <= 2^tau below fp16's largest value 65504: tau <= 15.
-    if (p.threshold <= kMaxTauF16)
-        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, COUNT, true>), dim3(p.num_tiles),
+    // The split exp2 is instantiated for the fp16 path with bf16 O and no
+    // counts only (the C ABI refuses other combinations).
+    if (p.threshold <= kMaxTauF16) {
+        if constexpr (!COUNT && std::is_same<OutT, unsigned short>::value) {
+            const dim3 g(p.num_tiles), b(Tile<D>::NT);
+            switch (p.exp2_poly) {
+                case 4: hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, false, true, 4>), g, b, 0, stream, p); return;
+                case 8: hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, false, true, 8>), g, b, 0, stream, p); return;
+                case 16: hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, false, true, 16>), g, b, 0, stream, p); return;
+                default: break;
+            }
+        }
+        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, COUNT, true, 0>), dim3(p.num_tiles),
                            dim3(Tile<D>::NT), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, COUNT, false>), dim3(p.num_tiles),
+    } else {
+        hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, VARLEN, OutT, COUNT, false, 0>), dim3(p.num_tiles),
                            dim3(Tile<D>::NT), 0, stream, p);
+    }
 }
 
 template <int D, bool CAUSAL, bool VARLEN, typename OutT>

@@ -47,6 +47,7 @@ struct FwdParams {
     uint32_t *rescale_counts; // nullptr, or per-row counts of reference moves (layout of lse)
     uint64_t *trace;          // timeline build only: event stamps, kTraceEvents per traced wave
     int trace_workgroups;     // ... of the first trace_workgroups workgroups (waves 0 and 4)
+    int exp2_poly;            // exponentials per 16 by the FMA polynomial: 0, 4, 8 or 16
 };
 
 // Timeline events (the trace build): code << 56 | shader clock.

@@ -115,6 +115,18 @@ typedef enum fa_schedule {
  *                       boundaries of the block loop; unused slots keep their
  *                       contents.  The default library returns
  *                       FA_ERR_UNSUPPORTED for a non-NULL trace.
+ *   exp2_poly         : 0 (the default), 4, 8 or 16: the split exp2 of
+ *                       "Flash Attention 4" (section "algorithm structure"),
+ *                       where part of the exponentials P = 2^x runs on the
+ *                       FMA pipes as 2^floor(x) * p(x - floor(x)), p a cubic
+ *                       of relative error below 7.5e-5 on [0, 1).  The value
+ *                       is how many of each 16 use the polynomial (evenly
+ *                       spread), the rest the hardware exp2.  Supported with
+ *                       bf16 O, rescale_threshold <= 15 and no
+ *                       rescale_counts (FA_ERR_UNSUPPORTED otherwise).  Off
+ *                       by default: on gfx950 the transcendental unit is
+ *                       faster per element than the polynomial's eight VALU
+ *                       instructions.
  */
 typedef struct fa_fwd_opts {
     int32_t o_dtype;
@@ -124,6 +136,7 @@ typedef struct fa_fwd_opts {
     uint32_t *rescale_counts;
     uint64_t *trace;
     int32_t trace_workgroups;
+    int32_t exp2_poly;
 } fa_fwd_opts;
 
 /* Fill *opts with the defaults (bf16 O, tau = 8, automatic schedule, Hkv = H,

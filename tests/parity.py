@@ -44,7 +44,7 @@ def to_device(w):
     return q, k, v, off
 
 
-def run_gpu(w, *, tau=8.0, o_dtype=None, schedule=0, tensors=None):
+def run_gpu(w, *, tau=8.0, o_dtype=None, schedule=0, tensors=None, exp2_poly=0):
     """Run the HIP path on workload w; returns (o float64 numpy, lse float64 numpy)."""
     import torch
     import flashattention_forward_fa_amd as fa
@@ -53,7 +53,7 @@ def run_gpu(w, *, tau=8.0, o_dtype=None, schedule=0, tensors=None):
         o_dtype = fa.FA_DTYPE_F32 if w.o_dtype == "f32" else fa.FA_DTYPE_BF16
     o, lse = fa.attention(q, k, v, w.scale, w.causal, varlen_offsets=off,
                           max_seqlen=w.Nq if w.varlen else None, o_dtype=o_dtype,
-                          rescale_threshold=tau, schedule=schedule)
+                          rescale_threshold=tau, schedule=schedule, exp2_poly=exp2_poly)
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy()
 

@@ -249,3 +249,30 @@ def test_library_binds_after_torch():
                        cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_exp2_poly_option_checks():
+    """exp2_poly: 0, 4, 8 or 16; nonzero needs tau <= 15 (fp16 P), bf16 O and no
+    rescale counts."""
+    P = 1 << 20
+    opts = fa.fa_fwd_opts_default()
+    assert opts.exp2_poly == 0
+    chk = lambda o: fa.fa_fwd_check(P, P, P, P, P, 1, 2, 64, 64, 128, 0.1, 1, None, o)
+    opts.exp2_poly = 8
+    assert chk(opts) == fa.FA_OK
+    for good in (4, 16):
+        opts.exp2_poly = good
+        assert chk(opts) == fa.FA_OK
+    for bad in (2, 12, 32, -1):
+        opts.exp2_poly = bad
+        assert chk(opts) == fa.FA_ERR_UNSUPPORTED
+    opts.exp2_poly = 8
+    opts.o_dtype = fa.FA_DTYPE_F32
+    assert chk(opts) == fa.FA_ERR_UNSUPPORTED
+    opts.o_dtype = fa.FA_DTYPE_BF16
+    opts.exp2_poly = 8
+    opts.rescale_threshold = 20.0
+    assert chk(opts) == fa.FA_ERR_UNSUPPORTED
+    opts.rescale_threshold = 8.0
+    opts.rescale_counts = P
+    assert chk(opts) == fa.FA_ERR_UNSUPPORTED

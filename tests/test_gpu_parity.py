@@ -379,3 +379,38 @@ def test_config(n):
                 else:
                     assert np.array_equal(o[:, 0], v0[:, 0])
             del o, lse
+
+
+# ------------------------------------------------------------ split exp2 (opt-in)
+
+@pytest.mark.parametrize("n", [3, 5])
+def test_exp2_poly_configs(n):
+    """Half of the exponentials by the FMA polynomial (fa_fwd_opts.exp2_poly = 8):
+    every element of the headline (d = 128) and the packed (d = 64) workloads,
+    both thresholds, bf16 O, at the same bar as the default path."""
+    w = wl.config(n)
+    q, k, v = parity.inputs_f64(w)
+    if w.varlen:
+        o_ref, lse_ref = oracle.attention_varlen(q, k, v, w.offsets, w.scale, w.causal)
+    else:
+        o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
+    del q, k, v
+    t = parity.to_device(w)
+    for tau in (8.0, 0.0):
+        label = f"config {n} {w.name} tau={tau:g} bf16 O, exp2 poly 8/16"
+        o, lse = parity.run_gpu(w, tau=tau, tensors=t, exp2_poly=8)
+        stats = parity.compare(o, lse, o_ref, lse_ref, bf16_out=True, what=label, label=label)
+        print(f"{label}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("shape", SMALL[:8], ids=lambda s: "B{}H{}q{}k{}d{}{}".format(*s[:5], "c" if s[5] else "f"))
+def test_exp2_poly_small(shape):
+    """Ragged tails, Nq != Nk, rows without keys (P of masked keys exactly 0 on
+    the polynomial path too), for each share of polynomial exponentials."""
+    B, H, Nq, Nk, d, causal = shape
+    w = wl.make_fixed(B, H, Nq, Nk, d, seed=B * 1000 + Nq + Nk + d + 7, causal=causal)
+    q, k, v = parity.inputs_f64(w)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
+    for ep in (4, 8, 16):
+        o, lse = parity.run_gpu(w, exp2_poly=ep)
+        parity.compare(o, lse, o_ref, lse_ref, bf16_out=True, what=f"{w.name} exp2 poly {ep}/16")
