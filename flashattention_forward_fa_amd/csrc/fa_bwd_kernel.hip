@@ -296,6 +296,9 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     // Row reads (A operand, 32 keys x 16 dims: key lq, chunk 2ds+g) and
     // transpose reads (K^T operand, as the forward's V^T).
     LdsOffsets lo = lds_offsets<D>(lane);
+    f32x16 negd;   // -D_i in every register: the start of each dP^T chain
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negd[i] = -dsum;
 
     if (nblocks > 0) {
         load(0);
@@ -314,11 +317,14 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
                 // S^T = K Q^T and dP^T = V dO^T for the 64 keys (32 per tile kt;
                 // 32-row tiles are 32 rows apart in the swizzled layout: the
                 // swizzle depends on the row within 16, unchanged by +32).
+                // The dP^T chain starts from -D_i, so it yields dP - D.
                 f32x16 s[NKT], dp[NKT];
 #pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
+                for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) { s[kt][i] = 0.f; dp[kt][i] = 0.f; }
+                    for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+                    dp[kt] = negd;
+                }
 #pragma unroll
                 for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
@@ -349,7 +355,7 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
                                 const int kt = ks >> 1;
                                 const int key = 32 * kt + 8 * (i >> 2) + (i & 3);   // relative to kv0 + 4g
                                 const float pr = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c, -lse2));
-                                const float v = pr * (dp[kt][i] - dsum);
+                                const float v = pr * dp[kt][i];
                                 if constexpr (decltype(masked)::value)
                                     v2[h2] = key > lim ? 0.f : v;
                                 else
@@ -407,7 +413,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     constexpr int CH = (NCHUNK + kBwdThreads - 1) / kBwdThreads;   // ... per thread
     constexpr bool EXACT = NCHUNK % kBwdThreads == 0;  // else the last round is partial
     __shared__ __attribute__((aligned(16))) unsigned short smem[4 * TILE + kBwdRows * D];
-    __shared__ __attribute__((aligned(16))) float rowt[2][2][BQ];   // [buf][lse2, D][query]
+    __shared__ __attribute__((aligned(16))) float rowt[2][2][BQ];   // [buf][lse2, -D][query]
     // Q block in buffer b at smem + b * TILE, dO block at smem + (2 + b) * TILE,
     // the workgroup's V rows at smem + 4 * TILE (read as B operands of dP).
 
@@ -518,7 +524,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             *(u32x4 *)(smem + (2 + buf) * TILE + st_off[rr]) = oreg[rr];
         }
         if (w == 0)
-            rowt[buf][lane / BQ][lane & (BQ - 1)] = lane < BQ ? tl * 1.4426950408889634f : td;
+            rowt[buf][lane / BQ][lane & (BQ - 1)] = lane < BQ ? tl * 1.4426950408889634f : -td;
     };
 
     LdsOffsets lo = lds_offsets<D>(lane);
@@ -542,9 +548,19 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
             const int qfirst = qb * BQ;
             // Every wave runs every block; pairs outside the mask get P = dS = 0.
             {
+                // The dP chain starts from -D of each register's query (the
+                // float4s of rowt are four consecutive queries, registers
+                // i0..i0+3), so it yields dP - D.
+                const float4 *lrow = (const float4 *)rowt[buf][0];
+                const float4 *drow = (const float4 *)rowt[buf][1];
                 f32x16 s, dp;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const float4 d4 = drow[(8 * i4 + 4 * g) >> 2];
+                    dp[4 * i4] = d4.x; dp[4 * i4 + 1] = d4.y; dp[4 * i4 + 2] = d4.z; dp[4 * i4 + 3] = d4.w;
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
                 for (int ds = 0; ds < NDS; ++ds) {
                     const bf16x8 qa = *(const bf16x8 *)(Qs + lo.row(ds));
@@ -562,8 +578,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                 // sequence, key in the sequence and, when causal, not after the query).
                 // Values formed for dropped pairs may be inf or NaN; the select
                 // replaces their bits without reading them as numbers.
-                const float4 *lrow = (const float4 *)rowt[buf][0];
-                const float4 *drow = (const float4 *)rowt[buf][1];
                 u32x4 pwv[NQS], swv[NQS];
 #pragma unroll
                 for (int qs = 0; qs < NQS; ++qs) {
@@ -571,14 +585,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
                     for (int hh = 0; hh < 2; ++hh) {
                         const int i0 = 8 * qs + 4 * hh;         // registers i0..i0+3
                         const float4 l4 = lrow[(8 * (i0 >> 2) + 4 * g) >> 2];
-                        const float4 d4 = drow[(8 * (i0 >> 2) + 4 * g) >> 2];
                         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
                         float pv[4], sv[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             pv[e] = __builtin_amdgcn_exp2f(fmaf(s[i0 + e], c, -lv[e]));
-                            sv[e] = pv[e] * (dp[i0 + e] - dvv[e]);
+                            sv[e] = pv[e] * dp[i0 + e];
                         }
                         pwv[qs][2 * hh] = pack_bf16x2(pv[0], pv[1]);
                         pwv[qs][2 * hh + 1] = pack_bf16x2(pv[2], pv[3]);
