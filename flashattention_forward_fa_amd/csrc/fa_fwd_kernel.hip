@@ -722,7 +722,37 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     const float l = lane_pair_sum(lsum);
     const float l32 = lane_pair_sum(lsum32);
     const float inv = l > 0.f ? ldexpf(1.f / l, vk) : 0.f;
-    if (row_ok) {
+    if constexpr (sizeof(OutT) == 2 && T::PINGPONG) {
+        // bf16 O through LDS (d = 128): each wave puts its 32 x D tile into
+        // the K/V buffers, free after the barrier below (16-byte chunks
+        // XOR-swizzled by row, so the 8-byte writes of 32 rows meet at most
+        // 2-way bank conflicts and the 16-byte reads none), and reads it back
+        // by rows, so that each store instruction writes four whole rows of O
+        // (16 lanes per row) instead of 16 bytes of each of 32 rows.  fp32 O
+        // (twice the bytes) does not fit the buffers; at d = 64 the other
+        // workgroups on the CU hide the direct stores, which then measure
+        // faster.  Both store from the accumulator layout.
+        constexpr int CPR = D / 8;                     // 16-byte chunks per row
+        __syncthreads();                               // every wave is past its last K/V read
+        unsigned short *Os = smem + w * 32 * D;
+#pragma unroll
+        for (int dt = 0; dt < T::NDT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int ch = 4 * dt + i4;
+                const float o0 = oacc[dt][4 * i4 + 0] * inv, o1 = oacc[dt][4 * i4 + 1] * inv;
+                const float o2 = oacc[dt][4 * i4 + 2] * inv, o3 = oacc[dt][4 * i4 + 3] * inv;
+                *(uint2 *)(Os + lq * D + ((ch ^ (lq & (CPR - 1))) << 3) + 4 * g) =
+                    make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+            }
+        unsigned short *Ob = (unsigned short *)p.o + ((int64_t)tc.q_tok0 + qw0) * tok + tc.h * D;
+#pragma unroll
+        for (int it = 0; it < 32 * CPR / 64; ++it) {
+            const int u = 64 * it + lane, r = u / CPR, cc = u % CPR;
+            const uint4 x = *(const uint4 *)(Os + r * D + ((cc ^ (r & (CPR - 1))) << 3));
+            if (qw0 + r < Nq) *(uint4 *)(Ob + (int64_t)r * tok + 8 * cc) = x;
+        }
+    } else if (row_ok) {
         OutT *Og = (OutT *)p.o + ((int64_t)tc.q_tok0 + qrow) * tok + tc.h * D;
 #pragma unroll
         for (int dt = 0; dt < T::NDT; ++dt)
@@ -739,6 +769,8 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
                     *(uint2 *)((unsigned short *)Og + d0) = v2;
                 }
             }
+    }
+    if (row_ok) {
         if (g == 0) {
             const float lse = l32 > 0.f ? logf(l32) + r * p.scale : -INFINITY;
             int64_t idx;

@@ -12,6 +12,10 @@ over the steady-state blocks of the traced waves (medians, shader cycles):
                global loads ("loads"), masking and softmax; then the barrier
   slot      -- one phase of the ping-pong: the SIMD's two waves are in
                opposite phases, so a block takes two slots per wave
+  prologue  -- from the wave's start to its first M phase (Q fragments,
+               first K/V block); epilogue -- from the end of the block loop to
+               the end (normalisation, O and LSE stores); with their sum over
+               the traced waves as a share of the waves' whole time
 
 and the matrix-core share of a slot (the MFMA cycles one M phase issues).  The
 stamps themselves wait for the wave's outstanding LDS and scalar operations,
@@ -111,7 +115,17 @@ def summarise(waves, d: int):
     """Medians over steady-state phases (the first and last two of each wave's
     M and V phases dropped)."""
     m_work, m_wait, v_store, v_load, v_soft, v_wait, v_work, slots = ([] for _ in range(8))
+    pro, epi = [], []
+    edge = total = 0
     for ev in waves:
+        codes = [c for c, _ in ev]
+        if codes and codes[0] == 1 and codes[-1] == 9 and 2 in codes and 8 in codes:
+            t_first_m = ev[codes.index(2)][1]
+            t_loop_end = ev[len(codes) - 1 - codes[::-1].index(8)][1]
+            pro.append(t_first_m - ev[0][1])
+            epi.append(ev[-1][1] - t_loop_end)
+            edge += pro[-1] + epi[-1]
+            total += ev[-1][1] - ev[0][1]
         m_beg = [i for i, (c, _) in enumerate(ev) if c == 2]
         v_beg = [i for i, (c, _) in enumerate(ev) if c == 4]
         for a in m_beg[2:-2]:
@@ -132,7 +146,8 @@ def summarise(waves, d: int):
     return {"slot": med(slots), "m_work": med(m_work), "m_wait": med(m_wait),
             "v_work": med(v_work), "v_stores": med(v_store), "v_loads": med(v_load),
             "v_softmax": med(v_soft), "v_wait": med(v_wait), "mfma_per_block": mfma,
-            "n_slots": len(slots), "n_waves": len(waves)}
+            "n_slots": len(slots), "n_waves": len(waves), "prologue": med(pro),
+            "epilogue": med(epi), "edge_share": edge / total if total else float("nan")}
 
 
 def main():
@@ -155,6 +170,8 @@ def main():
     print(f"           LDS writes {st['v_stores']:6.0f}   load issue {st['v_loads']:6.0f}   "
           f"mask + softmax {st['v_softmax']:6.0f}")
     print(f"  matrix-core share of a slot: {st['mfma_per_block'] / st['slot']:.3f}")
+    print(f"  prologue {st['prologue']:6.0f}   epilogue {st['epilogue']:6.0f}   "
+          f"(their share of the traced waves' time: {st['edge_share']:.3f})")
 
 
 if __name__ == "__main__":

@@ -15,7 +15,10 @@ load coordinates, swizzle addresses and MMA coverage on the host:
   converted to bf16, supplies P^T for O^T += V^T P^T;
 * the two half-waves that lane_pair_max / lane_pair_sum combine (lanes l and
   l ^ 32) hold complementary halves of one query's keys, and the causal mask's
-  key index is the accumulator's.
+  key index is the accumulator's;
+* the bf16 epilogue's LDS staging of O (d = 128) returns every element at its
+  own row and column, with conflict-free reads, 2-way writes, and store steps
+  that each cover whole rows.
 
 The swizzle and the K row pad are read from the kernel sources, so a change
 there is checked here; the lane address formulas are the kernel's, restated.
@@ -262,3 +265,77 @@ def test_model_sees_conflicts_without_the_swizzle(D, monkeypatch):
     monkeypatch.setattr(__import__(__name__), "KPAD", 0)
     assert sum(conflicts([(2 * k_read(D, l, 0, ds), 16) for l in range(64)], 16)
                for ds in range(D // 16)) > 0
+
+
+# ----------------------------------------------------------------- O staging (bf16 epilogue)
+
+def o_stage_write(D, lane, dt, i4):
+    """Element offset of the 4 bf16 of O a lane writes into its wave's staging
+    tile: row lq, head-dim columns 32*dt + 8*i4 + 4*g .. +3, the 16-byte chunk
+    4*dt + i4 XOR-swizzled by the row."""
+    lq, g = lane & 31, lane >> 5
+    cpr = D // 8
+    return lq * D + (((4 * dt + i4) ^ (lq & (cpr - 1))) << 3) + 4 * g
+
+
+def o_stage_read(D, lane, it):
+    """(row, chunk, element offset) of the 16 bytes a lane reads back in step it."""
+    cpr = D // 8
+    u = 64 * it + lane
+    r, cc = divmod(u, cpr)
+    return r, cc, r * D + ((cc ^ (r & (cpr - 1))) << 3)
+
+
+@pytest.mark.parametrize("D", [128])
+def test_o_staging_round_trip(D):
+    """Every element of the 32 x D tile is written once and read back at its
+    own row and column; the reads cover every row's chunks once."""
+    tile = np.full(32 * D, -1, dtype=np.int64)
+    for lane in range(64):
+        lq, g = lane & 31, lane >> 5
+        for dt in range(D // 32):
+            for i4 in range(4):
+                off = o_stage_write(D, lane, dt, i4)
+                for e in range(4):
+                    assert tile[off + e] == -1
+                    tile[off + e] = lq * D + 32 * dt + 8 * i4 + 4 * g + e   # its (row, column)
+    assert np.all(tile >= 0)
+    seen = set()
+    for it in range(32 * (D // 8) // 64):
+        for lane in range(64):
+            r, cc, off = o_stage_read(D, lane, it)
+            assert 0 <= r < 32 and (r, cc) not in seen
+            seen.add((r, cc))
+            assert list(tile[off:off + 8]) == [r * D + 8 * cc + e for e in range(8)]
+    assert len(seen) == 32 * (D // 8)
+
+
+@pytest.mark.parametrize("D", [128])
+def test_o_staging_banks(D):
+    """Reads (16 bytes, 16 lanes at a time) are conflict-free; the 8-byte
+    writes (32 lanes at a time, all in the same half of their chunks) cost
+    one extra cycle per group: 2-way, the least for 32 half-chunk writes."""
+    for it in range(32 * (D // 8) // 64):
+        acc = [(2 * o_stage_read(D, l, it)[2], 16) for l in range(64)]
+        assert conflicts(acc, 16) == 0
+    for dt in range(D // 32):
+        for i4 in range(4):
+            acc = [(2 * o_stage_write(D, l, dt, i4), 8) for l in range(64)]
+            assert conflicts(acc, 32) == 2
+
+
+@pytest.mark.parametrize("D", [128])
+def test_o_staged_stores_write_whole_rows(D):
+    """Each read-back step's lanes hold whole rows in order: the lanes of a
+    row are consecutive and their 16-byte pieces tile the row."""
+    cpr = D // 8
+    for it in range(32 * cpr // 64):
+        rows = defaultdict(list)
+        for lane in range(64):
+            r, cc, _ = o_stage_read(D, lane, it)
+            rows[r].append((lane, cc))
+        assert len(rows) == 64 // cpr
+        for r, lc in rows.items():
+            lanes = [l for l, _ in lc]
+            assert lanes == list(range(lanes[0], lanes[0] + cpr))
+            assert [c for _, c in lc] == list(range(cpr))

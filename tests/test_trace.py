@@ -28,6 +28,9 @@ def test_summary_of_a_synthetic_timeline():
     assert st["v_stores"] == 300 and st["v_loads"] == 200 and st["v_softmax"] == 1400
     assert st["v_work"] == 1900 and st["v_wait"] == 100
     assert st["mfma_per_block"] == 1024
+    # start at 0, first M phase at 100; loop end at 100 + 20 slots, end 50 later
+    assert st["prologue"] == 100 and st["epilogue"] == 50
+    assert st["edge_share"] == 150 / (100 + 20 * 2000 + 50)
 
 
 def test_stamps_decode():
