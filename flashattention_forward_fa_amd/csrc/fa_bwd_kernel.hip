@@ -103,7 +103,7 @@ struct BwdTile {
     int L_q, L_k;        // query and key lengths of the sequence
 };
 
-// Tiles of kBwdRows rows along a sequence: (b, h, m) from the workgroup index t.
+// Tiles of ROWS rows along a sequence: (b, h, m) from the workgroup index t.
 // heads = the head count of the owning dimension.  The order is tile-position
 // major, every (b, h) at one position before the next, so that with causal
 // masking the heaviest tiles start first (longest-processing-time order): the
@@ -111,6 +111,7 @@ struct BwdTile {
 // from the top), the dK/dV tile m visits the query blocks from m to the end
 // (reverse = false).  Packed sequences with a head count that is a multiple of
 // 8 use the XCD-aware order below; otherwise the order is by position only.
+template <int ROWS>
 __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads, int len_max,
                                            bool reverse, BwdTile &c) {
     if (p.offsets && heads % kNumXcd == 0) {
@@ -126,7 +127,7 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
         int base = 0;
         for (int b0 = 0; b0 < p.B; b0 += 64) {
             const int bb = b0 + lane;
-            const int nblk = bb < p.B ? (off[bb + 1] - off[bb] + kBwdRows - 1) / kBwdRows : 0;
+            const int nblk = bb < p.B ? (off[bb + 1] - off[bb] + ROWS - 1) / ROWS : 0;
             const int v = nblk * HX;
             int incl = v;
 #pragma unroll
@@ -152,7 +153,7 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
         }
         return false;
     }
-    const int nm = (len_max + kBwdRows - 1) / kBwdRows;
+    const int nm = (len_max + ROWS - 1) / ROWS;
     const int nbh = p.B * heads;
     c.m = t / nbh;
     if (reverse) c.m = nm - 1 - c.m;
@@ -163,7 +164,7 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
         c.tok0 = p.offsets[c.b];
         c.L_q = c.L_k = p.offsets[c.b + 1] - c.tok0;
         const int len = c.L_q;
-        return c.m * kBwdRows < len;
+        return c.m * ROWS < len;
     }
     c.tok0 = 0;
     c.L_q = p.Nq;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     // K block in buffer b at smem + b * TILE, V block at smem + (2 + b) * TILE.
 
     BwdTile tc;
-    if (!bwd_decode(blockIdx.x, p, p.H, p.Nq, CAUSAL, tc)) return;
+    if (!bwd_decode<kBwdRows>(blockIdx.x, p, p.H, p.Nq, CAUSAL, tc)) return;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     // the workgroup's V rows at smem + 4 * TILE (read as B operands of dP).
 
     BwdTile tc;
-    if (!bwd_decode(blockIdx.x, p, p.Hkv, p.Nk, false, tc)) return;   // tc.h is the K/V head
+    if (!bwd_decode<kBwdRows>(blockIdx.x, p, p.Hkv, p.Nk, false, tc)) return;   // tc.h is the K/V head
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, lq = lane & 31, g = lane >> 5;
