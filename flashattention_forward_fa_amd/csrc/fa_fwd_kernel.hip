@@ -115,15 +115,29 @@ struct TileCoord {
     int Nq, Nk;   // this sequence's lengths
 };
 
+constexpr int kLptHeadGroup = 4;   // heads per group of the fixed-length longest-first order
+
 __device__ __forceinline__ bool decode_fixed(int t, const FwdParams &p, TileCoord &c) {
     const int BH = p.B * p.H;
     const int nm = p.num_m;
     int bh, m;
     if (BH % kNumXcd == 0) {
         // Workgroup t runs on XCD t % 8; XCD x owns heads [x*HX, (x+1)*HX).
+        // Longest first, the XCD's heads in groups of kLptHeadGroup: all tiles
+        // of one group (longest first across its heads) before the next
+        // group's, so that the K/V of about that many heads, not of all HX,
+        // is read at a time and stays in the XCD's L2; the next group's
+        // longest tiles still start while the first group's short ones run.
         const int x = t % kNumXcd, u = t / kNumXcd, HX = BH / kNumXcd;
-        if (p.lpt) { m = nm - 1 - u / HX; bh = x * HX + u % HX; }
-        else       { bh = x * HX + u / nm; m = u % nm; }
+        if (p.lpt) {
+            const int gs = HX % kLptHeadGroup == 0 ? kLptHeadGroup : HX;
+            const int grp = u / (gs * nm), v = u % (gs * nm);
+            m = nm - 1 - v / gs;
+            bh = x * HX + grp * gs + v % gs;
+        } else {
+            bh = x * HX + u / nm;
+            m = u % nm;
+        }
     } else {
         if (p.lpt) { m = nm - 1 - t / BH; bh = t % BH; }
         else       { bh = t / nm; m = t % nm; }

@@ -233,12 +233,14 @@ def test_varlen_equals_separate_calls():
 
 def test_schedules_agree_bitwise():
     """Tile order changes which workgroup computes a tile, never its arithmetic."""
-    w = wl.make_fixed(2, 8, 600, 600, 128, seed=3, causal=True)
-    t = parity.to_device(w)
-    ref = parity.run_gpu(w, schedule=0, tensors=t)
-    for sch in (1, 2):
-        got = parity.run_gpu(w, schedule=sch, tensors=t)
-        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), sch
+    # 16 (batch, head) pairs: two per XCD; 64: eight per XCD, in two head groups
+    for H in (8, 32):
+        w = wl.make_fixed(2, H, 600, 600, 128, seed=3, causal=True)
+        t = parity.to_device(w)
+        ref = parity.run_gpu(w, schedule=0, tensors=t)
+        for sch in (1, 2):
+            got = parity.run_gpu(w, schedule=sch, tensors=t)
+            assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (H, sch)
     wv = wl.make_varlen(3, 64, seed=4, lengths=[900, 10, 300, 513], causal=True)
     tv = parity.to_device(wv)
     ref = parity.run_gpu(wv, schedule=2, tensors=tv)

@@ -1,0 +1,68 @@
+"""CPU model of the forward's fixed-length tile order (the kernel's decode_fixed,
+restated): workgroup t runs on XCD t % 8, and when B*H is a multiple of 8 the
+tiles it is given belong to that XCD's heads; longest first (causal), the
+XCD's heads go in groups whose tiles run longest first before the next
+group's.  Checked here: every (head, query tile) is given to exactly one
+workgroup, each XCD keeps to its own heads, and inside each head group the
+query-tile index never increases ("Flash Attention 4", section on tile
+scheduling: LPT order, and the L2 sections of heads)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "flashattention_forward_fa_amd", "csrc", "fa_fwd_kernel.hip")
+XCD = 8
+
+
+def _head_group():
+    with open(SRC) as f:
+        return int(re.search(r"constexpr int kLptHeadGroup = (\d+);", f.read()).group(1))
+
+
+GROUP = _head_group()
+
+
+def decode(t, BH, nm, lpt):
+    if BH % XCD == 0:
+        x, u, HX = t % XCD, t // XCD, BH // XCD
+        if lpt:
+            gs = GROUP if HX % GROUP == 0 else HX
+            grp, v = divmod(u, gs * nm)
+            return x * HX + grp * gs + v % gs, nm - 1 - v // gs
+        return x * HX + u // nm, u % nm
+    if lpt:
+        return t % BH, nm - 1 - t // BH
+    return t // nm, t % nm
+
+
+@pytest.mark.parametrize("BH", [1, 3, 8, 16, 24, 64, 72, 128, 256])
+@pytest.mark.parametrize("nm", [1, 3, 16])
+@pytest.mark.parametrize("lpt", [0, 1])
+def test_every_tile_once_and_xcd_heads(BH, nm, lpt):
+    seen = set()
+    for t in range(BH * nm):
+        bh, m = decode(t, BH, nm, lpt)
+        assert 0 <= bh < BH and 0 <= m < nm
+        assert (bh, m) not in seen
+        seen.add((bh, m))
+        if BH % XCD == 0:
+            HX = BH // XCD
+            assert bh // HX == t % XCD          # the XCD's own heads
+    assert len(seen) == BH * nm
+
+
+@pytest.mark.parametrize("BH", [64, 128, 256])
+def test_groups_run_longest_first(BH):
+    nm = 16
+    HX = BH // XCD
+    gs = GROUP if HX % GROUP == 0 else HX
+    for x in range(XCD):
+        order = [decode(x + XCD * u, BH, nm, 1) for u in range(HX * nm)]
+        for g0 in range(0, len(order), gs * nm):
+            block = order[g0:g0 + gs * nm]
+            heads = {bh for bh, _ in block}
+            assert len(heads) == gs                          # one group of heads at a time
+            ms = [m for _, m in block]
+            assert ms == sorted(ms, reverse=True)            # longest first inside it
