@@ -103,14 +103,16 @@ struct BwdTile {
     int L_q, L_k;        // query and key lengths of the sequence
 };
 
+constexpr int kBwdHeadGroup = 4;   // (batch, head) pairs per group of the fixed-length order
+
 // Tiles of ROWS rows along a sequence: (b, h, m) from the workgroup index t.
 // heads = the head count of the owning dimension.  The order is tile-position
 // major, every (b, h) at one position before the next, so that with causal
 // masking the heaviest tiles start first (longest-processing-time order): the
 // dQ tile m visits m + 1 key tiles' worth of blocks (reverse = true walks m
 // from the top), the dK/dV tile m visits the query blocks from m to the end
-// (reverse = false).  Packed sequences with a head count that is a multiple of
-// 8 use the XCD-aware order below; otherwise the order is by position only.
+// (reverse = false).  With a pair (packed: head) count that is a multiple of
+// 8 the order is XCD-aware (below); otherwise it is by position only.
 template <int ROWS>
 __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads, int len_max,
                                            bool reverse, BwdTile &c) {
@@ -155,9 +157,23 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
     }
     const int nm = (len_max + ROWS - 1) / ROWS;
     const int nbh = p.B * heads;
-    c.m = t / nbh;
+    int bh;
+    if (!p.offsets && nbh % kNumXcd == 0) {
+        // Fixed length: XCD x = t % 8 owns the (batch, head) pairs x + 8k; its
+        // tiles go in groups of kBwdHeadGroup pairs, each group's tiles
+        // position-major (heaviest first) before the next group's, so that the
+        // streamed K/V (dQ) or Q/dO (dK/dV) of about that many heads, not of
+        // all the XCD's, is read at a time and stays in its L2.
+        const int x = t % kNumXcd, u = t / kNumXcd, HX = nbh / kNumXcd;
+        const int gs = HX % kBwdHeadGroup == 0 ? kBwdHeadGroup : HX;
+        const int grp = u / (gs * nm), v = u % (gs * nm);
+        c.m = v / gs;
+        bh = x + kNumXcd * (grp * gs + v % gs);
+    } else {
+        c.m = t / nbh;
+        bh = t % nbh;
+    }
     if (reverse) c.m = nm - 1 - c.m;
-    const int bh = t % nbh;
     c.b = bh / heads;
     c.h = bh % heads;
     if (p.offsets) {

@@ -1,5 +1,5 @@
-"""CPU model of the forward's fixed-length tile order (the kernel's decode_fixed,
-restated): workgroup t runs on XCD t % 8, and when B*H is a multiple of 8 the
+"""CPU model of the fixed-length tile orders (the forward's decode_fixed and the
+backward's bwd_decode, restated).  Forward: workgroup t runs on XCD t % 8, and when B*H is a multiple of 8 the
 tiles it is given belong to that XCD's heads; longest first (causal), the
 XCD's heads go in groups whose tiles run longest first before the next
 group's.  Checked here: every (head, query tile) is given to exactly one
@@ -66,3 +66,54 @@ def test_groups_run_longest_first(BH):
             assert len(heads) == gs                          # one group of heads at a time
             ms = [m for _, m in block]
             assert ms == sorted(ms, reverse=True)            # longest first inside it
+
+
+# ----------------------------------------------------------------- backward
+
+BSRC = os.path.join(ROOT, "flashattention_forward_fa_amd", "csrc", "fa_bwd_kernel.hip")
+
+
+def _bwd_group():
+    with open(BSRC) as f:
+        return int(re.search(r"constexpr int kBwdHeadGroup = (\d+);", f.read()).group(1))
+
+
+BGROUP = _bwd_group()
+
+
+def bwd_decode_fixed(t, nbh, nm, reverse):
+    """The backward's fixed-length order (bwd_decode without offsets)."""
+    if nbh % XCD == 0:
+        x, u, HX = t % XCD, t // XCD, nbh // XCD
+        gs = BGROUP if HX % BGROUP == 0 else HX
+        grp, v = divmod(u, gs * nm)
+        m, bh = v // gs, x + XCD * (grp * gs + v % gs)
+    else:
+        m, bh = t // nbh, t % nbh
+    return bh, (nm - 1 - m if reverse else m)
+
+
+@pytest.mark.parametrize("nbh", [1, 6, 8, 16, 24, 64, 128])
+@pytest.mark.parametrize("nm", [1, 5, 32])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_every_tile_once(nbh, nm, reverse):
+    seen = set()
+    for t in range(nbh * nm):
+        bh, m = bwd_decode_fixed(t, nbh, nm, reverse)
+        assert 0 <= bh < nbh and 0 <= m < nm and (bh, m) not in seen
+        seen.add((bh, m))
+        if nbh % XCD == 0:
+            assert bh % XCD == t % XCD              # the XCD's own pairs
+    assert len(seen) == nbh * nm
+
+
+def test_bwd_groups_heaviest_first():
+    nbh, nm = 64, 32
+    for reverse in (False, True):
+        for x in range(XCD):
+            order = [bwd_decode_fixed(x + XCD * u, nbh, nm, reverse) for u in range(nbh // XCD * nm)]
+            for g0 in range(0, len(order), BGROUP * nm):
+                block = order[g0:g0 + BGROUP * nm]
+                assert len({bh for bh, _ in block}) == BGROUP
+                ms = [m for _, m in block]
+                assert ms == sorted(ms, reverse=reverse)   # dQ from the top, dK/dV from 0
