@@ -19,7 +19,10 @@ over the steady-state blocks of the traced waves (medians, shader cycles):
 
 and the matrix-core share of a slot (the MFMA cycles one M phase issues).  The
 stamps themselves wait for the wave's outstanding LDS and scalar operations,
-so absolute phase lengths are a little above the untraced kernel's.
+so absolute phase lengths are a little above the untraced kernel's; and each
+stamp is a global store, which the vector-memory counter counts like a load,
+so a section that waits for the staged K/V loads ("LDS writes") also waits
+for the stamps stored before it and reads long.
 
     python -m flashattention_forward_fa_amd.trace [--config 3] [--workgroups 256]
 """
