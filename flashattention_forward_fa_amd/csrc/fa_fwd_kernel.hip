@@ -533,22 +533,40 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
         };
 
         auto pv = [&](const unsigned short *Vs) {
+            // All V^T fragments read into their own registers, with AHEAD of
+            // them (two transpose reads each) in flight ahead of the MFMAs:
+            // left alone, the compiler recycled one register quad and waited
+            // out the LDS latency before every MFMA.
+            constexpr int NR = T::NKS * T::NDT;
+            constexpr int AHEAD = NR < 8 ? NR : 8;
+            i16x8 vf[T::NKS][T::NDT];
 #pragma unroll
-            for (int ks = 0; ks < T::NKS; ++ks) {
+            for (int ks = 0; ks < T::NKS; ++ks)
 #pragma unroll
                 for (int dt = 0; dt < T::NDT; ++dt) {
                     const unsigned short *a0 = Vs + 16 * ks * D;
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][0]));
                     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + v_off[dt][1]));
-                    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    vf[ks][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+            for (int ks = 0; ks < T::NKS; ++ks)
+#pragma unroll
+                for (int dt = 0; dt < T::NDT; ++dt) {
                     if constexpr (F16)
                         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(f16x8, both), __builtin_bit_cast(f16x8, pf[ks]), oacc[dt], 0, 0, 0);
+                            __builtin_bit_cast(f16x8, vf[ks][dt]), __builtin_bit_cast(f16x8, pf[ks]), oacc[dt], 0, 0, 0);
                     else
                         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, both), __builtin_bit_cast(bf16x8, pf[ks]), oacc[dt], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8, vf[ks][dt]), __builtin_bit_cast(bf16x8, pf[ks]), oacc[dt], 0, 0, 0);
                 }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);     // LDS reads
+#pragma unroll
+            for (int i = 0; i < NR - AHEAD; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
         };
 
         // Online softmax of one masked block: row max, rescale decision,
