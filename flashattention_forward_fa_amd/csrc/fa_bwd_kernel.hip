@@ -342,15 +342,35 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
                     for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
                     dp[kt] = negd;
                 }
+                {
+                    // Each K and V fragment in its own registers, RA steps of
+                    // reads in flight ahead of the MFMAs (left alone, the
+                    // compiler reused one register pair and waited out the
+                    // LDS latency before every pair of MFMAs).
+                    constexpr int NR = NDS * NKT, RA = NR < 3 ? NR : 3;
+                    bf16x8 kfr[NDS][NKT], vfr[NDS][NKT];
 #pragma unroll
-                for (int ds = 0; ds < NDS; ++ds)
+                    for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-                    for (int kt = 0; kt < NKT; ++kt) {
-                        const bf16x8 kf = *(const bf16x8 *)(Ks + lo.row(ds) + 32 * kt * D);
-                        const bf16x8 vf = *(const bf16x8 *)(Vs + lo.row(ds) + 32 * kt * D);
-                        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ds], s[kt], 0, 0, 0);
-                        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[ds], dp[kt], 0, 0, 0);
+                        for (int kt = 0; kt < NKT; ++kt) {
+                            kfr[ds][kt] = *(const bf16x8 *)(Ks + lo.row(ds) + 32 * kt * D);
+                            vfr[ds][kt] = *(const bf16x8 *)(Vs + lo.row(ds) + 32 * kt * D);
+                        }
+#pragma unroll
+                    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+                        for (int kt = 0; kt < NKT; ++kt) {
+                            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[ds][kt], qf[ds], s[kt], 0, 0, 0);
+                            dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[ds][kt], of[ds], dp[kt], 0, 0, 0);
+                        }
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RA, 0);      // LDS reads
+#pragma unroll
+                    for (int i = 0; i < NR - RA; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMAs
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                     }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * RA, 0);
+                }
                 // dS^T = P^T (dP^T - D), masked keys -> 0; to bf16 B operands.  A
                 // block every pair of which is kept skips the test (wave-uniform).
                 const int kv0 = kb * BN;
@@ -386,18 +406,33 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
                 };
                 if (full) frags(std::false_type{});
                 else      frags(std::true_type{});
-                // dQ^T += K^T dS^T.
+                // dQ^T += K^T dS^T (K^T fragments read ahead as above).
+                {
+                    constexpr int NR2 = NKS * NDT, RB = NR2 < 4 ? NR2 : 4;
+                    i16x8 ktf[NKS][NDT];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
+                    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const unsigned short *a0 = Ks + 16 * ks * D;
-                        const i16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + lo.tr(dt, 0)));
-                        const i16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + lo.tr(dt, 1)));
-                        const i16x8 both = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both),
-                                                                          sf[ks], acc[dt], 0, 0, 0);
+                        for (int dt = 0; dt < NDT; ++dt) {
+                            const unsigned short *a0 = Ks + 16 * ks * D;
+                            const i16x4 tlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + lo.tr(dt, 0)));
+                            const i16x4 thi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0 + lo.tr(dt, 1)));
+                            ktf[ks][dt] = __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        }
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                        for (int dt = 0; dt < NDT; ++dt)
+                            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ktf[ks][dt]),
+                                                                              sf[ks], acc[dt], 0, 0, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RB, 0);
+#pragma unroll
+                    for (int i = 0; i < NR2 - RB; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                     }
+                    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+                }
             }
             if (kb + 1 < nblocks) store(buf ^ 1);
             __syncthreads();
