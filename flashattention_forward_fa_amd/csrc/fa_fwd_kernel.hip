@@ -264,16 +264,18 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     if (!ok) return;   // uniform over the workgroup
 
 #ifdef FA_TRACE
-    // Timeline build: lane 0 of waves 0 and 4 (one per ping-pong group) of the
-    // first trace_workgroups workgroups records (event code << 56 | shader
-    // clock) at every phase boundary into p.trace, kTraceEvents slots per
-    // wave.  Reading the clock waits for this wave's outstanding LDS and
-    // scalar operations, so the build is a measurement tool, not the product.
+    // Timeline build: lane 0 of every wave of the first trace_workgroups
+    // workgroups records (event code << 56 | shader clock) at the phase
+    // boundaries of the block loop into p.trace, kTraceEvents slots per wave
+    // and kTraceWaves waves per workgroup.  Reading the clock waits for the
+    // wave's outstanding LDS and scalar operations; at a phase boundary there
+    // are none left to wait for (the barrier has just passed, or the phase's
+    // last MFMA or exponential has been issued), so the stamps leave the
+    // phases' lengths almost as they are.  A measurement tool, not the product.
     uint64_t *trace_out = nullptr;
     int trace_n = 0;
-    if (p.trace && (int)blockIdx.x < p.trace_workgroups && (threadIdx.x & 63) == 0 &&
-        ((threadIdx.x >> 6) & 3) == 0)
-        trace_out = p.trace + ((int64_t)blockIdx.x * 2 + (threadIdx.x >> 8)) * kTraceEvents;
+    if (p.trace && (int)blockIdx.x < p.trace_workgroups && (threadIdx.x & 63) == 0)
+        trace_out = p.trace + ((int64_t)blockIdx.x * kTraceWaves + (threadIdx.x >> 6)) * kTraceEvents;
     auto mark = [&](unsigned code) {
         if (trace_out && trace_n < kTraceEvents)
             trace_out[trace_n++] = ((uint64_t)code << 56) | ((uint64_t)clock64() & 0x00FFFFFFFFFFFFFFull);
@@ -649,10 +651,8 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
             mark(kTraceVBegin);
             if (j + 1 + grp < n) store_k(Kw);
             if (j + grp < n) store_v(Vw);
-            mark(kTraceVStored);
             load_k(j + 2 + grp);     // range 0 (reads nothing) past the last block
             load_v(j + 1 + grp);
-            mark(kTraceVLoaded);
             if (j >= 0 && j < n && active(j)) {
                 mask_block(j);
                 softmax();

@@ -50,11 +50,14 @@ struct FwdParams {
     int exp2_poly;            // exponentials per 16 by the FMA polynomial: 0, 4, 8 or 16
 };
 
-// Timeline events (the trace build): code << 56 | shader clock.
+// Timeline events (the trace build): code << 56 | shader clock, kTraceEvents
+// slots for each of kTraceWaves waves per traced workgroup (d = 64 uses the
+// first four).
 constexpr int kTraceEvents = 1024;
+constexpr int kTraceWaves = 8;
 enum TraceEvent : unsigned {
-    kTraceStart = 1, kTraceMBegin = 2, kTraceMEnd = 3, kTraceVBegin = 4, kTraceVStored = 5,
-    kTraceVLoaded = 6, kTraceVEnd = 7, kTraceLoopEnd = 8, kTraceEnd = 9
+    kTraceStart = 1, kTraceMBegin = 2, kTraceMEnd = 3, kTraceVBegin = 4, kTraceVEnd = 7,
+    kTraceLoopEnd = 8, kTraceEnd = 9
 };
 
 // Enqueue the forward kernel; returns a hipError_t value (0 = success).

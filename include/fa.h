@@ -108,12 +108,13 @@ typedef enum fa_schedule {
  *   trace, trace_workgroups : NULL / 0 (the defaults).  Only the timeline
  *                       build of the library (libfa_trace.so, compiled with
  *                       FA_TRACE) accepts a trace buffer: device memory,
- *                       8-byte aligned, of trace_workgroups * 2 * 1024 uint64,
- *                       owned by the caller.  Lane 0 of waves 0 and 4 of each
- *                       of the first trace_workgroups workgroups writes up to
- *                       1024 stamps (event << 56 | shader clock) at the phase
- *                       boundaries of the block loop; unused slots keep their
- *                       contents.  The default library returns
+ *                       8-byte aligned, of trace_workgroups * 8 * 1024 uint64,
+ *                       owned by the caller.  Lane 0 of every wave w (0..7;
+ *                       0..3 at d = 64) of each of the first trace_workgroups
+ *                       workgroups writes up to 1024 stamps (event << 56 |
+ *                       shader clock) at the phase boundaries of the block loop
+ *                       into slots [(wg * 8 + w) * 1024, +1024); unused slots
+ *                       keep their contents.  The default library returns
  *                       FA_ERR_UNSUPPORTED for a non-NULL trace.
  *   exp2_poly         : 0 (the default), 4, 8 or 16: the split exp2 of
  *                       "Flash Attention 4" (section "algorithm structure"),

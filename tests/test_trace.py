@@ -11,34 +11,60 @@ import flashattention_forward_fa_amd as fa
 from flashattention_forward_fa_amd import trace
 
 
-def _synthetic_wave(slot=2000, m_work=1500, stores=300, loads=200, soft=1400, blocks=10):
-    ev, t = [(1, 0)], 100
-    for _ in range(blocks):
-        ev += [(2, t), (3, t + m_work)]
-        t += slot
-        ev += [(4, t), (5, t + stores), (6, t + stores + loads), (7, t + stores + loads + soft)]
-        t += slot
-    ev += [(8, t), (9, t + 50)]
-    return ev
+def _synthetic_workgroup(slot=2000, m_work=(1500, 1600), v_work=(1900, 1800), blocks=10):
+    """Eight waves of a ping-pong workgroup: group 0 starts with M(0), group 1
+    with V(-1); every phase starts at its slot's start."""
+    waves = []
+    for wv in range(8):
+        g = wv // 4
+        ev, t = [(1, 0)], 100
+        kinds = (["M", "V"] if g == 0 else ["V", "M"]) * blocks
+        for kind in kinds:
+            if kind == "M":
+                ev += [(2, t), (3, t + m_work[g])]
+            else:
+                ev += [(4, t), (7, t + v_work[g])]
+            t += slot
+        ev += [(8, t), (9, t + 50)]
+        waves.append(ev)
+    return waves
 
 
 def test_summary_of_a_synthetic_timeline():
-    st = trace.summarise([_synthetic_wave(), _synthetic_wave()], d=128)
-    assert st["slot"] == 2000 and st["m_work"] == 1500 and st["m_wait"] == 500
-    assert st["v_stores"] == 300 and st["v_loads"] == 200 and st["v_softmax"] == 1400
-    assert st["v_work"] == 1900 and st["v_wait"] == 100
-    assert st["mfma_per_block"] == 1024
-    # start at 0, first M phase at 100; loop end at 100 + 20 slots, end 50 later
-    assert st["prologue"] == 100 and st["epilogue"] == 50
-    assert st["edge_share"] == 150 / (100 + 20 * 2000 + 50)
+    st = trace.summarise([_synthetic_workgroup(), _synthetic_workgroup()], d=128)
+    assert st["slot"] == 2000
+    assert st["m_work_g0"] == 1500 and st["v_work_g0"] == 1900
+    assert st["m_work_g1"] == 1600 and st["v_work_g1"] == 1800
+    # slots alternate between (group 0 M, group 1 V): slowest 1800, and
+    # (group 0 V, group 1 M): slowest 1900
+    assert st["slowest_work"] == 1850 and st["overhead"] == 150
+    assert st["mfma_per_block"] == 1024 and st["n_waves"] == 16
+    # start at 0, first M phase at 100 (group 0) or 2100 (group 1); loop end
+    # 20 slots after 100, end 50 later
+    assert st["epilogue"] == 50
+    assert st["edge_share"] == (4 * 150 + 4 * 2150) / (8 * (100 + 20 * 2000 + 50))
+
+
+def test_summary_of_a_synthetic_timeline_one_group():
+    waves = []
+    for _ in range(4):
+        ev, t = [(1, 0)], 100
+        for _ in range(10):
+            ev += [(2, t), (3, t + 700), (4, t + 720), (7, t + 1600)]
+            t += 1700
+        ev += [(8, t), (9, t + 50)]
+        waves.append(ev)
+    st = trace.summarise([waves], d=64)
+    assert st["slot"] == 1700 and st["m_work_g0"] == 700 and st["v_work_g0"] == 880
+    assert st["slowest_work"] == 1600 and st["overhead"] == 100
 
 
 def test_stamps_decode():
     row = np.zeros(trace.EVENTS, dtype=np.uint64)
     row[0] = (np.uint64(1) << np.uint64(56)) | np.uint64(12345)
     row[1] = (np.uint64(2) << np.uint64(56)) | np.uint64(12400)
-    waves = trace.phases(row.reshape(1, 1, -1))
-    assert waves == [[(1, 12345), (2, 12400)]]
+    wgs = trace.phases(row.reshape(1, 1, -1))
+    assert wgs == [[[(1, 12345), (2, 12400)]]]
 
 
 def test_plain_library_refuses_a_trace_buffer():
@@ -60,16 +86,16 @@ def test_traced_launch():
     from tests import parity
     w = wl.make_fixed(1, 8, 1024, 1024, 128, seed=90, causal=True)
     stamps = trace.record(w, 8.0, workgroups=8, settle_s=0.05)
-    waves = trace.phases(stamps)
-    assert len(waves) == 16                       # waves 0 and 4 of 8 workgroups
-    for ev in waves:
+    wgs = trace.phases(stamps)
+    assert len(wgs) == 8 and all(len(waves) == 8 for waves in wgs)   # every wave of 8 workgroups
+    for ev in (ev for waves in wgs for ev in waves):
         codes = [c for c, _ in ev]
         t = [x for _, x in ev]
         assert codes[0] == 1 and codes[-1] == 9 and 8 in codes
         assert all(b >= a for a, b in zip(t, t[1:]))
         assert codes.count(2) == codes.count(3) and codes.count(4) == codes.count(7)
-    st = trace.summarise(waves, w.d)
-    assert st["slot"] > 0 and st["m_work"] >= st["mfma_per_block"] * 0.9
+    st = trace.summarise(wgs, w.d)
+    assert st["slot"] > 0 and st["slowest_work"] > 0 and st["m_work_g0"] > 0
     # the traced build computes what the plain one does
     o_plain, l_plain = parity.run_gpu(w)
     lib = trace.load_trace_lib()
