@@ -1,6 +1,7 @@
 """GPU unit tests of the forward kernel's row reductions (lane_pair_max,
 lane_pair_sum of fa_device.h), run in a test-only kernel that holds a score
-block in the forward kernel's accumulator layout.
+block in the forward kernel's accumulator layout; and of the dispatch order the
+XCD-aware tile orders rely on.
 
 The vectors are the page's ("FlashAttention：一次前向计算", qingsen, section
 "how the max of one row is found across threads", table 7, and section "sum
@@ -31,6 +32,9 @@ def unit():
     lib = ctypes.CDLL(LIB)
     lib.fa_unit_lane_reduce.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_unit_lane_reduce.restype = ctypes.c_int
+    lib.fa_unit_xcd_of_workgroups.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_void_p]
+    lib.fa_unit_xcd_of_workgroups.restype = ctypes.c_int
     return lib
 
 
@@ -61,3 +65,20 @@ def test_page_vectors(unit):
         row = S[lane & 31].astype(np.float64)
         assert got[lane, 0] == row.max()
         np.testing.assert_allclose(got[lane, 1], row.sum(), rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("big", [1, 0])
+def test_workgroups_run_on_xcd_of_their_index_mod_8(unit, big):
+    """The forward and backward tile orders give XCD x the tiles of the
+    workgroups b with b mod 8 = x, so that the tiles reading one head's K/V share
+    that XCD's L2.  That rests on the dispatcher sending workgroup b to XCD
+    b mod 8; the hardware register XCC_ID, read by every workgroup of grids of
+    several dispatch rounds (workgroups of the d = 128 forward kernel's size and
+    LDS, one per compute unit, and of the 256-thread kernels'), shows it does."""
+    import torch
+    n = 4096
+    out = torch.full((n,), 0xFFFF, dtype=torch.int32, device="cuda")
+    assert unit.fa_unit_xcd_of_workgroups(out.data_ptr(), n, big, None) == 0
+    torch.cuda.synchronize()
+    xcc = out.cpu().numpy().astype(np.int64)
+    assert np.array_equal(xcc, np.arange(n) % 8)
