@@ -117,7 +117,8 @@ template <int ROWS>
 __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads, int len_max,
                                            bool reverse, BwdTile &c) {
     if (p.offsets && heads % kNumXcd == 0) {
-        // Varlen: workgroup t runs on XCD t % 8, which owns heads
+        // Varlen: the workgroups t with one value of x = t % 8 share an XCD
+        // (round-robin dispatch), and they own heads
         // [x*HX, (x+1)*HX) of every sequence; on an XCD the tiles go sequence
         // by sequence, head by head, each head's tiles longest first, so the
         // tiles that read one head's K/V (or Q/dO) run together and share the
@@ -159,7 +160,8 @@ __device__ __forceinline__ bool bwd_decode(int t, const BwdParams &p, int heads,
     const int nbh = p.B * heads;
     int bh;
     if (!p.offsets && nbh % kNumXcd == 0) {
-        // Fixed length: XCD x = t % 8 owns the (batch, head) pairs x + 8k; its
+        // Fixed length: the workgroups with t % 8 = x (one XCD) own the
+        // (batch, head) pairs x + 8k; their
         // tiles go in groups of kBwdHeadGroup pairs, each group's tiles
         // position-major (heaviest first) before the next group's, so that the
         // streamed K/V (dQ) or Q/dO (dK/dV) of about that many heads, not of

@@ -122,7 +122,9 @@ __device__ __forceinline__ bool decode_fixed(int t, const FwdParams &p, TileCoor
     const int nm = p.num_m;
     int bh, m;
     if (BH % kNumXcd == 0) {
-        // Workgroup t runs on XCD t % 8; XCD x owns heads [x*HX, (x+1)*HX).
+        // Workgroups go round-robin over the 8 XCDs (from an XCD that depends
+        // on the launches before), so the workgroups t with one value of
+        // x = t % 8 share an XCD; they own heads [x*HX, (x+1)*HX).
         // Longest first, the XCD's heads in groups of kLptHeadGroup: all tiles
         // of one group (longest first across its heads) before the next
         // group's, so that the K/V of about that many heads, not of all HX,
@@ -162,7 +164,8 @@ __device__ __forceinline__ bool decode_varlen(int t, const FwdParams &p, TileCoo
     const int32_t *off = p.offsets;
     int b = -1, m = -1, h = 0;
     if (p.lpt && p.H % kNumXcd == 0) {
-        // Workgroup t runs on XCD t % 8, which owns query heads [x*HX, (x+1)*HX)
+        // The workgroups t with one value of x = t % 8 share an XCD (round-robin
+        // dispatch), and they own query heads [x*HX, (x+1)*HX)
         // of every sequence (an eighth of the work for any lengths).  On an
         // XCD the tiles go sequence by sequence, head by head, each head's
         // tiles longest first, so the tiles that read one head's K/V run

@@ -1,6 +1,7 @@
 """CPU model of the fixed-length tile orders (the forward's decode_fixed and the
-backward's bwd_decode, restated).  Forward: workgroup t runs on XCD t % 8, and when B*H is a multiple of 8 the
-tiles it is given belong to that XCD's heads; longest first (causal), the
+backward's bwd_decode, restated).  Forward: the workgroups t with one value of
+t % 8 run on one XCD (round-robin dispatch), and when B*H is a multiple of 8 the
+tiles they are given belong to that XCD's heads; longest first (causal), the
 XCD's heads go in groups whose tiles run longest first before the next
 group's.  Checked here: every (head, query tile) is given to exactly one
 workgroup, each XCD keeps to its own heads, and inside each head group the
