@@ -345,6 +345,23 @@ def test_grouped_full_size(tau):
 
 # ------------------------------------------------------------ the five configurations
 
+_REFS = {}
+
+
+def _config_reference(n):
+    """The fp64 oracle's O and LSE of configuration n over the whole workload,
+    computed once per session (the default-path and the split-exp2 tests of a
+    configuration compare against the same reference)."""
+    if n not in _REFS:
+        w = wl.config(n)
+        q, k, v = parity.inputs_f64(w)
+        if w.varlen:
+            _REFS[n] = oracle.attention_varlen(q, k, v, w.offsets, w.scale, w.causal)
+        else:
+            _REFS[n] = oracle.attention(q, k, v, w.scale, w.causal)
+    return _REFS[n]
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_config(n):
     """Every element of O and LSE of the five measured workloads, at full size in
@@ -353,12 +370,7 @@ def test_config(n):
     the workload's O type and the other one (fp32 O holds the arithmetic to the
     plain bar; bf16 O is what the benchmark times)."""
     w = wl.config(n)
-    q, k, v = parity.inputs_f64(w)
-    if w.varlen:
-        o_ref, lse_ref = oracle.attention_varlen(q, k, v, w.offsets, w.scale, w.causal)
-    else:
-        o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
-    del q, k, v
+    o_ref, lse_ref = _config_reference(n)
     t = parity.to_device(w)
     own = 1 if w.o_dtype == "f32" else 0
     for tau in (8.0, 0.0):
@@ -391,12 +403,7 @@ def test_exp2_poly_configs(n):
     every element of the headline (d = 128) and the packed (d = 64) workloads,
     both thresholds, bf16 O, at the same bar as the default path."""
     w = wl.config(n)
-    q, k, v = parity.inputs_f64(w)
-    if w.varlen:
-        o_ref, lse_ref = oracle.attention_varlen(q, k, v, w.offsets, w.scale, w.causal)
-    else:
-        o_ref, lse_ref = oracle.attention(q, k, v, w.scale, w.causal)
-    del q, k, v
+    o_ref, lse_ref = _config_reference(n)
     t = parity.to_device(w)
     for tau in (8.0, 0.0):
         label = f"config {n} {w.name} tau={tau:g} bf16 O, exp2 poly 8/16"
