@@ -1,7 +1,8 @@
 """GPU unit tests of the forward kernel's row reductions (lane_pair_max,
 lane_pair_sum of fa_device.h), run in a test-only kernel that holds a score
 block in the forward kernel's accumulator layout; and of the dispatch order the
-XCD-aware tile orders rely on.
+XCD-aware tile orders rely on; and a measurement of the issue rates behind
+the forward kernel's phase slot (printed).
 
 The vectors are the page's ("FlashAttention：一次前向计算", qingsen, section
 "how the max of one row is found across threads", table 7, and section "sum
@@ -35,6 +36,9 @@ def unit():
     lib.fa_unit_xcd_of_workgroups.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_void_p]
     lib.fa_unit_xcd_of_workgroups.restype = ctypes.c_int
+    lib.fa_unit_issue_rates.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_unit_issue_rates.restype = ctypes.c_int
     return lib
 
 
@@ -85,3 +89,32 @@ def test_workgroups_run_on_xcd_of_their_index_mod_8(unit, big):
     torch.cuda.synchronize()
     xcc = out.cpu().numpy().astype(np.int64)
     assert np.array_equal(xcc, (xcc[0] + np.arange(n)) % 8)
+
+
+def test_issue_rates(unit):
+    """Issue rates of the two waves of a SIMD, as the forward kernel's ping-pong
+    pairs them (one wave streaming 32x32x16 MFMAs, the other independent
+    v_fma_f32): cycles per MFMA and per v_fma_f32, each wave alone and side by
+    side.  Printed for the design notes; asserted only where the hardware
+    leaves no doubt (an MFMA takes its 8 passes, a wave64 v_fma_f32 at least
+    the 4 cycles of a 16-lane SIMD and at most that of the matrix core's)."""
+    import torch
+    grid, iters = 256, 2000
+    cycles = torch.zeros(grid * 8, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(grid * 512, dtype=torch.float32, device="cuda")
+    rates = {}
+    for name, ra, rb in (("mfma alone", 1, 0), ("fma alone", 0, 2), ("side by side", 1, 2)):
+        for _ in range(2):   # the first launch warms the clocks and caches
+            assert unit.fa_unit_issue_rates(cycles.data_ptr(), sink.data_ptr(), grid, iters, ra, rb,
+                                            None) == 0
+            torch.cuda.synchronize()
+        c = cycles.cpu().numpy().astype(np.float64).reshape(grid, 8)
+        rates[name] = (np.median(c[:, :4]) / (4 * iters), np.median(c[:, 4:]) / (32 * iters))
+    mfma_alone = rates["mfma alone"][0]
+    fma_alone = rates["fma alone"][1]
+    mfma_side, fma_side = rates["side by side"]
+    print(f"issue rates (shader cycles): v_mfma_f32_32x32x16_bf16 {mfma_alone:.1f} alone, "
+          f"{mfma_side:.1f} beside a v_fma_f32 wave; v_fma_f32 {fma_alone:.2f} alone, "
+          f"{fma_side:.2f} beside an MFMA wave", flush=True)
+    assert 30.0 <= mfma_alone <= 40.0 and 30.0 <= mfma_side <= 40.0
+    assert 4.0 <= fma_alone <= 32.0 and 4.0 <= fma_side <= 32.0
