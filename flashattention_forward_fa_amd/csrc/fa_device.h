@@ -38,6 +38,16 @@ __device__ __forceinline__ int vswz(int r) {
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+// The lane index, computed afresh: the mask passes through an empty asm, so
+// the compiler cannot reuse (and keep live) a lane index computed earlier.
+// Used where a lane-dependent value is needed only after or rarely inside a
+// long loop whose register budget is full.
+__device__ __forceinline__ int fresh_lane() {
+    unsigned m = ~0u;
+    asm volatile("" : "+s"(m));
+    return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
+}
+
 __device__ __forceinline__ float lane_pair_max(float x) {
     // Combine lanes l and l^32 (both halves see the maximum of the pair).
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

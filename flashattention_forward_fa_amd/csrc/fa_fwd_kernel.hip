@@ -257,6 +257,7 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     using T = Tile<D>;
     __shared__ __attribute__((aligned(16))) unsigned short smem[2 * T::K_ELEMS + 2 * T::V_ELEMS];
     __shared__ unsigned vmax_bits;   // workgroup max of |V| (bit pattern), overflow path only
+    __shared__ unsigned wave_bad[T::NW];   // per wave: a non-finite accumulator (overflow path)
     unsigned short *const Kbuf0 = smem;
     unsigned short *const Kbuf1 = smem + T::K_ELEMS;
     unsigned short *const Vbuf0 = smem + 2 * T::K_ELEMS;
@@ -299,7 +300,6 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     const int m0 = tc.m * T::BM;
     const int qw0 = m0 + 32 * w;          // first query row of this wave
     const int qrow = qw0 + lq;            // query row of this lane
-    const bool row_ok = qrow < Nq;
     const int64_t tok = (int64_t)p.H * D; // elements between consecutive Q/O tokens
     const int64_t tkv = (int64_t)p.Hkv * D;      // ... K/V tokens (grouped K/V heads)
     const unsigned tokb = (unsigned)(tok * 2);   // ... in bytes
@@ -491,8 +491,11 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
         const bool need_mask = (kv0 + T::BN > Nk) ||
                                (CAUSAL && kv0 + T::BN - 1 > qw0 + causal_shift);
         if (need_mask) {
-            // Lane's last usable key, relative to its first key in the block.
-            const int lim = (CAUSAL ? min(Nk - 1, qrow + causal_shift) : Nk - 1) - kv0 - 4 * g;
+            // Lane's last usable key, relative to its first key in the block
+            // (row and half from a fresh lane index: nothing lane-dependent
+            // is held across the loop for the rare masked block).
+            const int ln = fresh_lane();
+            const int lim = (CAUSAL ? min(Nk - 1, qw0 + (ln & 31) + causal_shift) : Nk - 1) - kv0 - 4 * (ln >> 5);
 #pragma unroll
             for (int kt = 0; kt < T::NKT; ++kt)
 #pragma unroll
@@ -728,12 +731,19 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
         for (int dt = 0; dt < T::NDT; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) t += oacc[dt][i];
-        if (!__builtin_amdgcn_readfirstlane(__syncthreads_or(!(fabsf(t) <= 3.4028235e38f)))) break;
+        // Any wave with a non-finite sum?  One LDS word per wave (every lane
+        // of a wave stores the same ballot result), one barrier.
+        wave_bad[w] = __ballot(!(fabsf(t) <= 3.4028235e38f)) != 0 ? 1u : 0u;
+        __syncthreads();
+        unsigned any_bad = 0u;
+#pragma unroll
+        for (int i = 0; i < T::NW; ++i) any_bad |= wave_bad[i];
+        if (!__builtin_amdgcn_readfirstlane(any_bad)) break;
         // Largest |V| over the tile's K/V blocks (rows past Nk read as 0).
         float vmax = 0.f;
         for (int kb = 0; kb < nblocks; ++kb) {
             const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)kb * T::BN * tkv, block_bytes(kb));
-            for (int u = tid; u < T::BN * D / 8; u += T::NT) {
+            for (int u = 64 * w + fresh_lane(); u < T::BN * D / 8; u += T::NT) {
                 const u32x4 x = buffer_load16(rv, (unsigned)(u / (D / 8)) * tkvb + 16u * (u % (D / 8)));
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -741,7 +751,7 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
                                              fabsf(__uint_as_float(x[e] & 0xFFFF0000u))));
             }
         }
-        if (tid == 0) vmax_bits = 0u;
+        if (w == 0 && fresh_lane() == 0) vmax_bits = 0u;
         __syncthreads();
         atomicMax(&vmax_bits, __float_as_uint(vmax));   // non-negative floats order as their bits
         __syncthreads();
@@ -753,7 +763,11 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     }
 
     mark(kTraceLoopEnd);
-    // Epilogue: O = o / l, LSE = ln l + r * scale.
+    // Epilogue: O = o / l, LSE = ln l + r * scale.  The lane-dependent
+    // values are computed again here rather than held across the loop.
+    const int elane = fresh_lane(), elq = elane & 31, eg = elane >> 5;
+    const int erow = qw0 + elq;
+    const bool erow_ok = erow < Nq;
     const float l = lane_pair_sum(lsum);
     const float l32 = lane_pair_sum(lsum32);
     const float inv = l > 0.f ? ldexpf(1.f / l, vk) : 0.f;
@@ -777,23 +791,23 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
                 const int ch = 4 * dt + i4;
                 const float o0 = oacc[dt][4 * i4 + 0] * inv, o1 = oacc[dt][4 * i4 + 1] * inv;
                 const float o2 = oacc[dt][4 * i4 + 2] * inv, o3 = oacc[dt][4 * i4 + 3] * inv;
-                *(uint2 *)(Os + lq * D + ((ch ^ (lq & (CPR - 1))) << 3) + 4 * g) =
+                *(uint2 *)(Os + elq * D + ((ch ^ (elq & (CPR - 1))) << 3) + 4 * eg) =
                     make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
             }
         unsigned short *Ob = (unsigned short *)p.o + ((int64_t)tc.q_tok0 + qw0) * tok + tc.h * D;
 #pragma unroll
         for (int it = 0; it < 32 * CPR / 64; ++it) {
-            const int u = 64 * it + lane, r = u / CPR, cc = u % CPR;
+            const int u = 64 * it + elane, r = u / CPR, cc = u % CPR;
             const uint4 x = *(const uint4 *)(Os + r * D + ((cc ^ (r & (CPR - 1))) << 3));
             if (qw0 + r < Nq) *(uint4 *)(Ob + (int64_t)r * tok + 8 * cc) = x;
         }
-    } else if (row_ok) {
-        OutT *Og = (OutT *)p.o + ((int64_t)tc.q_tok0 + qrow) * tok + tc.h * D;
+    } else if (erow_ok) {
+        OutT *Og = (OutT *)p.o + ((int64_t)tc.q_tok0 + erow) * tok + tc.h * D;
 #pragma unroll
         for (int dt = 0; dt < T::NDT; ++dt)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const int d0 = 32 * dt + 8 * i4 + 4 * g;
+                const int d0 = 32 * dt + 8 * i4 + 4 * eg;
                 const float o0 = oacc[dt][4 * i4 + 0] * inv, o1 = oacc[dt][4 * i4 + 1] * inv;
                 const float o2 = oacc[dt][4 * i4 + 2] * inv, o3 = oacc[dt][4 * i4 + 3] * inv;
                 if constexpr (sizeof(OutT) == 4) {
@@ -805,12 +819,12 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
                 }
             }
     }
-    if (row_ok) {
-        if (g == 0) {
+    if (erow_ok) {
+        if (eg == 0) {
             const float lse = l32 > 0.f ? logf(l32) + r * p.scale : -INFINITY;
             int64_t idx;
-            if (VARLEN) idx = (int64_t)tc.h * p.offsets[p.B] + tc.q_tok0 + qrow;
-            else        idx = ((int64_t)tc.b * p.H + tc.h) * Nq + qrow;
+            if (VARLEN) idx = (int64_t)tc.h * p.offsets[p.B] + tc.q_tok0 + erow;
+            else        idx = ((int64_t)tc.b * p.H + tc.h) * Nq + erow;
             p.lse[idx] = lse;
             if constexpr (COUNT) p.rescale_counts[idx] = nmoves;
         }

@@ -236,7 +236,8 @@ def test_mask_index_is_the_accumulator_key():
     lane's 4*(lane/32) already subtracted: the same key as s_key."""
     src = _read("fa_fwd_kernel.hip")
     assert "if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) s[kt][i] = -INFINITY;" in src
-    assert "- kv0 - 4 * g;" in src
+    assert "const int ln = fresh_lane();" in src
+    assert "- kv0 - 4 * (ln >> 5);" in src
     for l in range(64):
         for kt in range(2):
             for i in range(16):
