@@ -241,8 +241,12 @@ __global__ __launch_bounds__(kBwdThreads) void fa_bwd_dq_kernel(BwdParams p) {
     bf16x8 qf[NDS], of[NDS];
     float dpart = 0.f;
     {
+        // Descriptor ranges are wave-uniform; read back from lane 0 so that the
+        // descriptors stay scalar (the clamp compiles to a vector instruction,
+        // and a descriptor in vector registers makes every load a loop).
         const int rows = max(0, min(32, Nq - q0));
-        const unsigned bytes = rows > 0 ? (unsigned)(rows - 1) * tqb + (unsigned)(D * 2) : 0u;
+        const unsigned bytes = __builtin_amdgcn_readfirstlane(
+            rows > 0 ? (unsigned)(rows - 1) * tqb + (unsigned)(D * 2) : 0u);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qg + (int64_t)q0 * tq, bytes);
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(dOg + (int64_t)q0 * tq, bytes);
         const __amdgpu_buffer_rsrc_t rO = make_rsrc(Og_in + (int64_t)q0 * tq, bytes);
@@ -493,15 +497,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     bf16x8 kf[NDS];
     unsigned short *Vs = smem + 4 * TILE;
     {
+        // Wave-uniform descriptor ranges, read back from lane 0 (scalar descriptors).
         const int rows = max(0, min(32, Nk - k0w));
-        const unsigned bytes = rows > 0 ? (unsigned)(rows - 1) * tkvb + (unsigned)(D * 2) : 0u;
+        const unsigned bytes = __builtin_amdgcn_readfirstlane(
+            rows > 0 ? (unsigned)(rows - 1) * tkvb + (unsigned)(D * 2) : 0u);
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg + (int64_t)k0w * tkv, bytes);
         const unsigned off = (unsigned)lq * tkvb + (unsigned)(16 * g);
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds)
             kf[ds] = __builtin_bit_cast(bf16x8, buffer_load16(rk, off + 32u * ds));
         const int vrows = max(0, min(kBwdRows, Nk - tc.m * kBwdRows));
-        const unsigned vbytes = vrows > 0 ? (unsigned)(vrows - 1) * tkvb + (unsigned)(D * 2) : 0u;
+        const unsigned vbytes = __builtin_amdgcn_readfirstlane(
+            vrows > 0 ? (unsigned)(vrows - 1) * tkvb + (unsigned)(D * 2) : 0u);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg + (int64_t)tc.m * kBwdRows * tkv, vbytes);
         constexpr int VCH = kBwdRows * D / 8 / kBwdThreads;
 #pragma unroll

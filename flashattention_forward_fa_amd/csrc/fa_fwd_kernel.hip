@@ -299,7 +299,6 @@ __global__ __launch_bounds__(Tile<D>::NT, fwd_waves_per_simd(D)) void fa_fwd_ker
     const int Nq = tc.Nq, Nk = tc.Nk;
     const int m0 = tc.m * T::BM;
     const int qw0 = m0 + 32 * w;          // first query row of this wave
-    const int qrow = qw0 + lq;            // query row of this lane
     const int64_t tok = (int64_t)p.H * D; // elements between consecutive Q/O tokens
     const int64_t tkv = (int64_t)p.Hkv * D;      // ... K/V tokens (grouped K/V heads)
     const unsigned tokb = (unsigned)(tok * 2);   // ... in bytes
