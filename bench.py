@@ -26,6 +26,9 @@ Prints one JSON line:
                bracketing the K launches), against the bf16
                dense MFMA peak (2.5 PFLOP/s, nominal at 2.4 GHz), and against
                CUs x 4096 flop/clk x the measured shader clock (peak_at_sclk);
+               launch_ms_median / launch_ms_min: median and minimum of K more
+               launches, each between its own pair of events (the mean is
+               avg_launch_ms);
                traffic = HBM bytes per launch from the committed rocprofv3
                FETCH_SIZE / WRITE_SIZE summary (null unless it was taken on the
                kernel source as it is now)
@@ -287,6 +290,21 @@ def main():
     sclk_ghz = float((sm[-1, 0] - sm[0, 0]) / (sm[-1, 1] - sm[0, 1]) * ref_hz / 1e9)
     probe_ms = float((sm[-1, 1] - sm[0, 1]) / ref_hz * 1e3)
 
+    # Per-launch durations: K more launches, each between its own pair of
+    # events on the launch stream (the launches still queue back to back);
+    # their median and minimum beside the mean above.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in pairs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([e0.elapsed_time(e1) for e0, e1 in pairs])
+    launch_ms_median = float(np.median(per_launch))
+    launch_ms_min = float(per_launch.min())
+
     flops = w.flops() * (2.5 if args.backward else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
@@ -328,6 +346,9 @@ def main():
                      "frac_at_sclk": round(achieved / peak_at_sclk, 4),
                      "cus": cus,
                      "avg_launch_ms": round(avg_launch_ms, 5),
+                     "launch_ms_median": round(launch_ms_median, 5),
+                     "launch_ms_min": round(launch_ms_min, 5),
+                     "achieved_at_median": round(flops / (launch_ms_median * 1e-3) / 1e12, 2),
                      "algorithmic_hbm_bytes": w.io_bytes()},
     }
     if args.cpu_seconds > 0:
